@@ -1,0 +1,319 @@
+"""Plain CPU reference of the routed-expert FP8 grouped matmul (GMM) family.
+
+Test infrastructure only: nothing on the product path imports this module.  Only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it.  It shares no code with the HIP library.
+
+Every function restates the method of two pages:
+
+* P1 = "MoE: native FP8 QAT for routed-expert GMMs" (maxtext PR #5969):
+  Description ("What the new flags change"), Data flow (table), Implementation.
+* P3 = "MoE fp8 backward: in-kernel drhs operand quantization + configurable
+  gradient dtype" (maxtext PR #4971): What.
+
+Conventions (one reading each; the list of readings is kept with the design notes):
+
+* ``lhs`` is a static ragged buffer ``[M, K]`` of bf16 bit patterns (uint16).
+  Rows ``[off_g, off_g + size_g)`` belong to expert ``g`` with
+  ``off_g = sum(size_h, h < g)``; rows at or past ``sum(group_sizes)`` are stale
+  and never read.  Negative sizes count as 0 and the running sum is clamped to M.
+* Weight codes are ``[G, K, N]`` e4m3fn codes (uint8, N fastest); the weight
+  scale is one f32 per (expert, output channel), ``[G, N]``.
+* Quantities the pages fix in f32 (activation scale, the quotient x/s, the
+  dequantized weight before its bf16 rounding) are computed in f32; everything
+  else is float64.  The FP8 contraction itself is exact in float64: every e4m3
+  value is a multiple of 2^-9 and below 2^9, so for K <= 8192 every partial sum
+  is a multiple of 2^-18 below 2^31 and fits the 53-bit significand.
+* Results are returned for valid rows only; what a kernel leaves in the rows
+  past the valid prefix is checked separately (they must stay untouched).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import formats as F
+
+AMAX_FLOOR = np.float32(1e-12)
+E4M3_MAX = np.float32(448.0)
+
+
+# --------------------------------------------------------------------------- layout
+
+@dataclass
+class Layout:
+    """Row ranges of each expert in the static buffer.
+
+    ``start[g]``, ``end[g]``: valid rows of expert g are ``[start[g], end[g])``.
+    ``valid``: number of valid rows M_v.  ``clamped``/``negative`` report the
+    two repairs (sum past M, negative size).
+    """
+    start: np.ndarray
+    end: np.ndarray
+    valid: int
+    clamped: bool
+    negative: bool
+
+    def group_of_rows(self, M: int) -> np.ndarray:
+        """Expert id of each row, -1 for rows past the valid prefix."""
+        gid = np.full(M, -1, dtype=np.int64)
+        for g in range(len(self.start)):
+            gid[self.start[g]:self.end[g]] = g
+        return gid
+
+
+def layout(group_sizes, M: int) -> Layout:
+    """Group offsets from ``group_sizes`` (P3, What: the in-kernel path touches
+    only the tiles covered by group_sizes).  Negative sizes are treated as 0 and
+    the running sum is clamped to the static row count M, so no row index ever
+    leaves the buffer."""
+    gs = np.asarray(group_sizes, dtype=np.int64)
+    negative = bool(np.any(gs < 0))
+    gs = np.maximum(gs, 0)
+    ends_raw = np.cumsum(gs)
+    clamped = bool(len(gs) and ends_raw[-1] > M)
+    end = np.minimum(ends_raw, M)
+    start = np.concatenate([[0], end[:-1]]) if len(gs) else np.zeros(0, np.int64)
+    valid = int(end[-1]) if len(gs) else 0
+    return Layout(start.astype(np.int64), end.astype(np.int64), valid, clamped, negative)
+
+
+# --------------------------------------------------------------------------- forward
+
+def row_scales(x_f32: np.ndarray) -> np.ndarray:
+    """One f32 scale per activation row over the whole K axis:
+    ``s = max(amax, 1e-12) / 448`` evaluated in f32 (P1, Implementation: LHS
+    quantization options, lhs_f32_scale; the native forward always uses the full
+    K with an f32 scale)."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    return (np.maximum(amax, AMAX_FLOOR) / E4M3_MAX).astype(np.float32)
+
+
+def quantize_rows(x_f32: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """e4m3fn codes of ``x / s`` with the quotient rounded to f32 first (P1,
+    Description: the forward quantizes the activation inside the kernel)."""
+    q = (np.asarray(x_f32, np.float32) / np.asarray(s, np.float32)[:, None]).astype(np.float32)
+    return F.encode(q, F.E4M3)
+
+
+def _fwd_rows(x_bits, codes_g, scale_g):
+    """Exact f64 pre-rounding result ``(sum_k dec(q)*dec(c)) * s_row * scale``
+    for rows of one expert, plus the abs-sum bound term."""
+    x = F.bf16_to_f32(x_bits)
+    s = row_scales(x)
+    q = quantize_rows(x, s)
+    qd = F.decode(q, F.E4M3)
+    cd = F.decode(codes_g, F.E4M3)
+    acc = qd @ cd                                     # exact (see module doc)
+    y = (acc * s.astype(np.float64)[:, None]) * scale_g.astype(np.float64)[None, :]
+    absum = ((np.abs(qd) @ np.abs(cd)) * s.astype(np.float64)[:, None]) \
+        * np.abs(scale_g.astype(np.float64))[None, :]
+    return y, absum, q, s
+
+
+@dataclass
+class FwdResult:
+    rows: np.ndarray        # buffer row index of each result row
+    group: np.ndarray       # expert of each result row
+    y: np.ndarray           # f64 pre-rounding GEMM result [R, N] (scaled)
+    absum: np.ndarray       # s_row * |scale| * sum_k |dec q * dec c|   [R, N]
+    out: np.ndarray         # bf16 bits of the op's output [R, N or N/2]
+    out_f64: np.ndarray     # exact f64 value before the bf16 rounding
+    act_codes: np.ndarray   # e4m3 codes of the quantized rows [R, K]
+    act_scale: np.ndarray   # f32 row scales [R]
+
+
+def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """``silu(gate) * up`` in float64, silu(z) = z / (1 + exp(-z)) (P1,
+    Implementation: gmm_silu_fp8 is wi with a fused SwiGLU)."""
+    with np.errstate(over="ignore"):
+        return gate / (1.0 + np.exp(-gate)) * up
+
+
+def gmm_fwd(lhs_bits, codes, scale, group_sizes, *, swiglu_out=False, rows=None) -> FwdResult:
+    """Native FP8 forward GMM (P1, Description and Data flow table: wi/wo run
+    FP8 x FP8 with f32 accumulation, read the codes and per-channel scale, and
+    quantize the activation rows in the kernel).
+
+    ``rows``: optional subset of buffer rows to evaluate (each row is
+    independent given its own scale); default all valid rows.  With
+    ``swiglu_out`` the N columns are ``[gate | up]`` and the output is
+    ``bf16(silu(gate) * up)`` of width N/2 (P1, Implementation: gmm_silu_fp8).
+    """
+    lhs_bits = np.asarray(lhs_bits)
+    M, K = lhs_bits.shape
+    G, K2, N = codes.shape
+    assert K2 == K and scale.shape == (G, N)
+    lay = layout(group_sizes, M)
+    gid = lay.group_of_rows(M)
+    if rows is None:
+        rows = np.arange(lay.valid, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    assert np.all(gid[rows] >= 0), "requested rows must be valid rows"
+    R = len(rows)
+    y = np.zeros((R, N)); absum = np.zeros((R, N))
+    act_codes = np.zeros((R, K), np.uint8); act_scale = np.zeros(R, np.float32)
+    for g in range(G):
+        sel = np.nonzero(gid[rows] == g)[0]
+        if len(sel) == 0:
+            continue
+        yy, aa, q, s = _fwd_rows(lhs_bits[rows[sel]], codes[g], scale[g])
+        y[sel], absum[sel], act_codes[sel], act_scale[sel] = yy, aa, q, s
+    if swiglu_out:
+        assert N % 2 == 0
+        I = N // 2
+        out_f64 = swiglu(y[:, :I], y[:, I:])
+    else:
+        out_f64 = y
+    out = F.f64_to_bf16_bits(out_f64)
+    return FwdResult(rows, gid[rows], y, absum, out, out_f64, act_codes, act_scale)
+
+
+# --------------------------------------------------------------------------- dequant
+
+def dequantize(codes, scale) -> np.ndarray:
+    """``bf16(f32(dec(code) * scale))`` for ``codes[G,K,N]`` and ``scale[G,N]``
+    (P1, Implementation: dequantize_fp8_codes; the f32 product rounded once to
+    bf16).  Returns bf16 bit patterns [G, K, N]."""
+    w32 = F.decode(codes, F.E4M3).astype(np.float32) * np.asarray(scale, np.float32)[:, None, :]
+    return F.f64_to_bf16_bits(w32.astype(np.float32).astype(np.float64))
+
+
+# --------------------------------------------------------------------------- dLHS
+
+@dataclass
+class DlhsResult:
+    rows: np.ndarray
+    group: np.ndarray
+    y: np.ndarray        # f64 result before the bf16 rounding [R, K]
+    absum: np.ndarray    # sum_n |dout * w|   [R, K]
+    out: np.ndarray      # bf16 bits [R, K]
+
+
+def gmm_dlhs(dout_bits, codes, scale, group_sizes, *, rows=None) -> DlhsResult:
+    """Backward dLHS: ``dlhs[r, k] = bf16(sum_n dout[r, n] * w[g, k, n])`` with
+    ``w = dequantize(codes, scale)`` (P1, Description: the backward dLHS GMM
+    reads the codes and dequantizes each tile, bit-identical to the dequant
+    path; Implementation: the rhs_contract_dequant path).  The sum over n is
+    float64."""
+    dout_bits = np.asarray(dout_bits)
+    M, N = dout_bits.shape
+    G, K, N2 = codes.shape
+    assert N2 == N
+    lay = layout(group_sizes, M)
+    gid = lay.group_of_rows(M)
+    if rows is None:
+        rows = np.arange(lay.valid, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    assert np.all(gid[rows] >= 0)
+    R = len(rows)
+    y = np.zeros((R, K)); absum = np.zeros((R, K))
+    for g in range(G):
+        sel = np.nonzero(gid[rows] == g)[0]
+        if len(sel) == 0:
+            continue
+        w = F.bf16_to_f64(dequantize(codes[g:g + 1], scale[g:g + 1])[0])   # [K, N]
+        d = F.bf16_to_f64(dout_bits[rows[sel]])
+        y[sel] = d @ w.T
+        absum[sel] = np.abs(d) @ np.abs(w).T
+    return DlhsResult(rows, gid[rows], y, absum, F.f64_to_bf16_bits(y))
+
+
+# --------------------------------------------------------------------------- tgmm
+
+@dataclass
+class TgmmTile:
+    group: int
+    tile: int          # buffer-aligned tile index (rows [tile*tile_m, (tile+1)*tile_m))
+    row0: int          # first row of the tile within the group
+    row1: int          # one past the last row
+
+
+def tgmm_tiles(group_sizes, M: int, tile_m: int) -> list[TgmmTile]:
+    """Non-empty (expert, gm-tile) pairs in (expert, tile) order.  Tiles are
+    aligned to the buffer and intersected with each expert's rows, so a tile
+    that straddles an expert boundary gives one entry per expert (P3, What:
+    per-gm-tile-per-channel quantization that touches only the tiles covered
+    by group_sizes)."""
+    lay = layout(group_sizes, M)
+    out = []
+    for g in range(len(lay.start)):
+        a, b = int(lay.start[g]), int(lay.end[g])
+        if b <= a:
+            continue
+        for t in range(a // tile_m, (b - 1) // tile_m + 1):
+            out.append(TgmmTile(g, t, max(a, t * tile_m), min(b, (t + 1) * tile_m)))
+    return out
+
+
+def column_scales(x_f32: np.ndarray, fmax) -> np.ndarray:
+    """Per-channel f32 scale of one tile: ``max(amax over the tile's rows,
+    1e-12) / fmax`` in f32 (same formula as the forward row scale)."""
+    amax = np.max(np.abs(np.asarray(x_f32, np.float32)), axis=0)
+    return (np.maximum(amax, AMAX_FLOOR) / np.float32(fmax)).astype(np.float32)
+
+
+def quantize_cols(x_f32, s, fmt) -> np.ndarray:
+    q = (np.asarray(x_f32, np.float32) / np.asarray(s, np.float32)[None, :]).astype(np.float32)
+    return F.encode(q, fmt)
+
+
+#: decoded values times these factors are integers (multiples of 2^-9 / 2^-16)
+_INT_SHIFT = {F.E4M3: 9, F.E5M2: 16}
+
+
+@dataclass
+class TgmmResult:
+    drhs: np.ndarray            # f32 [G, Kc, Nc] (selected columns)
+    drhs_f64: np.ndarray        # f64 before the final f32 rounding
+    absum: np.ndarray           # sum_t sL sD sum_r |dec qL dec qD|
+    tiles: list                 # TgmmTile list (order of the scale rows)
+    sL: np.ndarray              # f32 [T, Kc]
+    sD: np.ndarray              # f32 [T, Nc]
+
+
+def tgmm_quant(lhs_bits, dout_bits, group_sizes, grad_fmt: str, tile_m: int = 512,
+               k_cols=None, n_cols=None) -> TgmmResult:
+    """Weight-gradient tgmm with in-kernel operand quantization:
+    ``drhs[g] = sum_t (sum_{r in T} dec(qL[r,:])^T dec(qD[r,:])) * (sL[t] x sD[t])``
+    where for each non-empty (expert, tile) pair T the lhs is quantized to e4m3
+    with one scale per lhs channel and dout to the gradient format with one
+    scale per dout channel, both over T's rows only (P3, What:
+    moe_bwd_inkernel_quant and bwd_quantization_dtype).  The tile sums are exact
+    integer sums; scaling and the sum over tiles are float64, rounded once to
+    f32.  An expert without rows gets exact zeros.
+
+    ``k_cols``/``n_cols`` restrict the output to some columns; every channel's
+    scale depends only on its own column, so the restriction is exact.
+    """
+    lhs_bits = np.asarray(lhs_bits); dout_bits = np.asarray(dout_bits)
+    M, K = lhs_bits.shape
+    M2, N = dout_bits.shape
+    assert M2 == M
+    G = len(group_sizes)
+    kc = np.arange(K) if k_cols is None else np.asarray(k_cols)
+    nc = np.arange(N) if n_cols is None else np.asarray(n_cols)
+    tiles = tgmm_tiles(group_sizes, M, tile_m)
+    acc = np.zeros((G, len(kc), len(nc)))
+    absum = np.zeros((G, len(kc), len(nc)))
+    sLs = np.zeros((len(tiles), len(kc)), np.float32)
+    sDs = np.zeros((len(tiles), len(nc)), np.float32)
+    fmax_g = F.FMAX[grad_fmt]
+    for i, tl in enumerate(tiles):
+        xl = F.bf16_to_f32(lhs_bits[tl.row0:tl.row1][:, kc])
+        xd = F.bf16_to_f32(dout_bits[tl.row0:tl.row1][:, nc])
+        sL = column_scales(xl, 448.0)
+        sD = column_scales(xd, fmax_g)
+        qL = quantize_cols(xl, sL, F.E4M3)
+        qD = quantize_cols(xd, sD, grad_fmt)
+        iL = (F.decode(qL, F.E4M3) * 2.0 ** _INT_SHIFT[F.E4M3]).astype(np.int64)
+        iD = (F.decode(qD, grad_fmt) * 2.0 ** _INT_SHIFT[grad_fmt]).astype(np.int64)
+        tile_sum = (iL.T @ iD).astype(np.float64) * 2.0 ** -(_INT_SHIFT[F.E4M3] + _INT_SHIFT[grad_fmt])
+        tile_abs = (np.abs(iL).T @ np.abs(iD)).astype(np.float64) * 2.0 ** -(_INT_SHIFT[F.E4M3] + _INT_SHIFT[grad_fmt])
+        outer = sL.astype(np.float64)[:, None] * sD.astype(np.float64)[None, :]
+        acc[tl.group] += tile_sum * outer
+        absum[tl.group] += tile_abs * outer
+        sLs[i], sDs[i] = sL, sD
+    return TgmmResult(acc.astype(np.float32), acc, absum, tiles, sLs, sDs)
