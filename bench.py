@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-expert FP8 grouped-matmul hot path on one MI355X.
+
+One step = one pass of every op of the path over the dropless per-device
+buffer of a DeepSeek-V3-like MoE layer (G=32 local experts, static buffer of
+32768 rows of which 19,661 are valid, Zipf(1.1)-skewed expert sizes with four
+empty experts, Inf/NaN garbage in the stale tail):
+
+  quantize_rows_fp8 + gmm_silu_fp8_q   wi forward, K=7168 -> 2x2048, SwiGLU
+  quantize_rows_fp8 + gmm_fp8_fwd_q    wo forward, K=2048 -> 7168
+  gmm_dlhs_fp8                         wo dLHS  (dout [.,7168] -> [.,2048])
+  gmm_dlhs_fp8                         wi dLHS  (dout [.,4096] -> [.,7168])
+  tgmm_quant (e5m2 gradient)           drhs [32, 7168, 2048] f32
+  dequantize_fp8_codes                 wo codes [32, 2048, 7168]
+
+Inputs are seeded synthetic data already resident in HBM.  `value` is the
+aggregate GEMM TFLOP/s of a step (flops of the five GEMMs over valid rows,
+divided by the step's wall time on the GPU, dequantization included).  HIP
+events recorded between the calls on the launch stream give each op's time;
+the bf16 arm (same scheduler, pre-dequantized weights) gives the FP8/bf16
+ratio; the CPU oracle is timed on a bounded sample on the host cores.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 (OCP) MFMA
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def make_inputs():
+    import workloads as W
+    t0 = time.time()
+    sh = W.SHAPES[3]
+    G, M, valid = sh["G"], sh["M"], sh["valid"]
+    gs = W.group_sizes(3)
+    d = {"gs": gs, "G": G, "M": M, "valid": valid}
+    d["codes_wi"], d["scale_wi"] = W.weights(3, W.W_WI, G, sh["K_wi"], sh["N_wi"])
+    d["codes_wo"], d["scale_wo"] = W.weights(3, W.W_WO, G, sh["K_wo"], sh["N_wo"])
+    d["lhs_wi"] = W.activations(3, W.LHS_WI, M, sh["K_wi"], valid, outlier_stream=W.OUTLIERS_WI)
+    d["lhs_wo"] = W.activations(3, W.LHS_WO, M, sh["K_wo"], valid, outlier_stream=W.OUTLIERS_WO)
+    d["dout_wi"] = W.gradients(3, W.DOUT_WI, M, sh["N_wi"], valid)
+    d["dout_wo"] = W.gradients(3, W.DOUT_WO, M, sh["N_wo"], valid)
+    t4 = W.make(4, "tgmm")
+    d["lhs_t"], d["dout_t"] = t4["lhs"], t4["dout"]
+    log(f"[bench] synthetic inputs generated in {time.time() - t0:.1f}s")
+    return d
+
+
+def flops_of(d):
+    mv = int(np.sum(d["gs"]))
+    return {
+        "wi_fwd": 2.0 * mv * 7168 * 4096,
+        "wo_fwd": 2.0 * mv * 2048 * 7168,
+        "wo_dlhs": 2.0 * mv * 7168 * 2048,
+        "wi_dlhs": 2.0 * mv * 4096 * 7168,
+        "tgmm": 2.0 * mv * 7168 * 2048,
+    }
+
+
+def bytes_of(d):
+    """Algorithmic HBM bytes per op: valid rows in and out, codes and scales of
+    non-empty experts, full outputs where the op writes them."""
+    mv = int(np.sum(d["gs"]))
+    ne = int(np.sum(np.asarray(d["gs"]) > 0))
+    G = d["G"]
+    return {
+        "wi_quant": mv * 7168 * (2 + 1) + mv * 4,
+        "wi_gemm": mv * 7168 + mv * 4 + ne * 7168 * 4096 * 1 + ne * 4096 * 4 + mv * 2048 * 2,
+        "wo_quant": mv * 2048 * (2 + 1) + mv * 4,
+        "wo_gemm": mv * 2048 + mv * 4 + ne * 2048 * 7168 + ne * 7168 * 4 + mv * 7168 * 2,
+        "wo_dlhs": mv * 7168 * 2 + ne * 2048 * 7168 + ne * 7168 * 4 + mv * 2048 * 2,
+        "wi_dlhs": mv * 4096 * 2 + ne * 7168 * 4096 + ne * 4096 * 4 + mv * 7168 * 2,
+        "tgmm": mv * (7168 + 2048) * 2 + G * 7168 * 2048 * 4,
+        "dequant": G * 2048 * 7168 * (1 + 2) + G * 7168 * 4,
+    }
+
+
+def cpu_baseline(d, seconds_target):
+    """The oracle as it stands, on a bounded sample: the wi forward (SwiGLU) of
+    evenly spread valid rows; returns its TFLOP/s on this host."""
+    from oracle import gmm as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    mv = int(np.sum(d["gs"]))
+    n = 128
+    while True:
+        rows = np.linspace(0, mv - 1, n).astype(np.int64)
+        t0 = time.time()
+        O.gmm_fwd(d["lhs_wi"], d["codes_wi"], d["scale_wi"], d["gs"], swiglu_out=True, rows=rows)
+        dt = time.time() - t0
+        if dt * 2 > seconds_target or n >= 4096:
+            break
+        n *= 2
+    fl = 2.0 * n * 7168 * 4096
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"wi forward + SwiGLU (K=7168, N=2x2048) of {n} of the {mv} valid rows, "
+                      f"spread over the experts; {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-arm", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_moe_grouped_amd as G
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    G.lib()
+
+    d = make_inputs()
+    gs = to_dev(d["gs"])
+    M = d["M"]
+    lhs_wi, lhs_wo = to_dev(d["lhs_wi"]), to_dev(d["lhs_wo"])
+    codes_wi, scale_wi = to_dev(d["codes_wi"]), to_dev(d["scale_wi"])
+    codes_wo, scale_wo = to_dev(d["codes_wo"]), to_dev(d["scale_wo"])
+    dout_wi, dout_wo = to_dev(d["dout_wi"]), to_dev(d["dout_wo"])
+    lhs_t, dout_t = to_dev(d["lhs_t"]), to_dev(d["dout_t"])
+    dev = lhs_wi.device
+    aq_wi = torch.empty((M, 7168), dtype=torch.uint8, device=dev)
+    as_wi = torch.empty((M,), dtype=torch.float32, device=dev)
+    aq_wo = torch.empty((M, 2048), dtype=torch.uint8, device=dev)
+    as_wo = torch.empty((M,), dtype=torch.float32, device=dev)
+    h = torch.empty((M, 2048), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, 7168), dtype=torch.bfloat16, device=dev)
+    dh = torch.empty((M, 2048), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, 7168), dtype=torch.bfloat16, device=dev)
+    drhs = torch.empty((32, 7168, 2048), dtype=torch.float32, device=dev)
+    ws_t = torch.empty(G.workspace_bytes(G.OP_TGMM, M, 7168, 2048, 32), dtype=torch.uint8, device=dev)
+    wdeq = torch.empty((32, 2048, 7168), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    names = ["wi_quant", "wi_gemm", "wo_quant", "wo_gemm", "wo_dlhs", "wi_dlhs", "tgmm", "dequant"]
+    calls = [
+        lambda: G.quantize_rows_fp8(lhs_wi, gs, codes=aq_wi, scales=as_wi),
+        lambda: G.gmm_silu_fp8_q(aq_wi, as_wi, codes_wi, scale_wi, gs, out=h),
+        lambda: G.quantize_rows_fp8(lhs_wo, gs, codes=aq_wo, scales=as_wo),
+        lambda: G.gmm_fp8_fwd_q(aq_wo, as_wo, codes_wo, scale_wo, gs, out=y),
+        lambda: G.gmm_dlhs_fp8(dout_wo, codes_wo, scale_wo, gs, out=dh),
+        lambda: G.gmm_dlhs_fp8(dout_wi, codes_wi, scale_wi, gs, out=dx),
+        lambda: G.tgmm_quant(lhs_t, dout_t, gs, "e5m2", 512, out=drhs, workspace=ws_t),
+        lambda: G.dequantize_fp8_codes(codes_wo, scale_wo, out=wdeq),
+    ]
+
+    def step(events=None):
+        for i, c in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            c()
+        if events is not None:
+            events[-1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(args.steps):
+        step(ev[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    op_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+             for i, n in enumerate(names)}
+
+    fl = flops_of(d)
+    by = bytes_of(d)
+    total_flops = sum(fl.values())
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    def tfs(f, ms):
+        return f / (ms * 1e-3) / 1e12
+
+    ops = {
+        "wi_fwd": {"ms": op_ms["wi_quant"] + op_ms["wi_gemm"], "tflops": tfs(fl["wi_fwd"], op_ms["wi_quant"] + op_ms["wi_gemm"]),
+                   "peak": FP8_PEAK_TFLOPS},
+        "wo_fwd": {"ms": op_ms["wo_quant"] + op_ms["wo_gemm"], "tflops": tfs(fl["wo_fwd"], op_ms["wo_quant"] + op_ms["wo_gemm"]),
+                   "peak": FP8_PEAK_TFLOPS},
+        "wo_dlhs": {"ms": op_ms["wo_dlhs"], "tflops": tfs(fl["wo_dlhs"], op_ms["wo_dlhs"]), "peak": BF16_PEAK_TFLOPS},
+        "wi_dlhs": {"ms": op_ms["wi_dlhs"], "tflops": tfs(fl["wi_dlhs"], op_ms["wi_dlhs"]), "peak": BF16_PEAK_TFLOPS},
+        "tgmm": {"ms": op_ms["tgmm"], "tflops": tfs(fl["tgmm"], op_ms["tgmm"]),
+                 "gbs": by["tgmm"] / (op_ms["tgmm"] * 1e-3) / 1e9},
+        "dequant": {"ms": op_ms["dequant"], "gbs": by["dequant"] / (op_ms["dequant"] * 1e-3) / 1e9},
+    }
+    for k in ("wi_fwd", "wo_fwd", "wo_dlhs", "wi_dlhs"):
+        ops[k]["frac_peak"] = ops[k]["tflops"] / ops[k]["peak"]
+    kern = {k: {"ms": op_ms[k]} for k in names}
+    for k in ("wi_gemm", "wo_gemm"):
+        f = fl["wi_fwd"] if k == "wi_gemm" else fl["wo_fwd"]
+        kern[k]["tflops"] = tfs(f, op_ms[k])
+        kern[k]["frac_fp8_peak"] = kern[k]["tflops"] / FP8_PEAK_TFLOPS
+    for k in ("wi_quant", "wo_quant", "dequant"):
+        kern[k]["gbs"] = by[k] / (op_ms[k] * 1e-3) / 1e9
+
+    # dominant kernel by time and its roofline
+    dom = max(names, key=lambda k: op_ms[k])
+    if dom in ("wi_gemm", "wo_gemm"):
+        f = fl["wi_fwd"] if dom == "wi_gemm" else fl["wo_fwd"]
+        roof = {"kernel": dom, "bound": "mfma", "achieved": tfs(f, op_ms[dom]), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif dom in ("wi_dlhs", "wo_dlhs"):
+        roof = {"kernel": dom, "bound": "mfma", "achieved": tfs(fl[dom], op_ms[dom]), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": by[dom] / (op_ms[dom] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+
+    # bf16 arm: same scheduler, weights dequantized beforehand (not timed)
+    ratio = None
+    if not args.no_bf16_arm:
+        w_wi = G.dequantize_fp8_codes(codes_wi, scale_wi)
+        w_wo = wdeq
+        ob_wi = torch.empty((M, 4096), dtype=torch.bfloat16, device=dev)
+
+        def timed(fn, n=10):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+
+        t_bf_wi = timed(lambda: G.gmm_bf16_fwd(lhs_wi, w_wi, gs, out=ob_wi))
+        t_bf_wo = timed(lambda: G.gmm_bf16_fwd(lhs_wo, w_wo, gs, out=y))
+        ratio = {"wi": t_bf_wi / ops["wi_fwd"]["ms"], "wo": t_bf_wo / ops["wo_fwd"]["ms"],
+                 "bf16_wi_ms": t_bf_wi, "bf16_wo_ms": t_bf_wo,
+                 "pages_tpu7x": {"wi": 1.635, "wo": 1.731}}
+        del w_wi
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, args.cpu_seconds)
+
+    line = {
+        "metric": "FP8 grouped-GEMM TFLOP/s (fwd wi/wo, bwd dLHS) and % of MI355X MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "DeepSeek-V3-like dropless per-device MoE step: G=32 experts, 32768-row buffer with "
+                        "19661 valid rows (Zipf 1.1, 4 empty experts, garbage tail); wi 7168->2x2048 SwiGLU, "
+                        "wo 2048->7168, dLHS wi+wo, tgmm 7168x2048 e5m2, dequantize wo codes",
+            "G": 32, "M": M, "valid_rows": int(np.sum(d["gs"])),
+            "gemm_tflop_per_step": round(total_flops / 1e12, 4),
+        },
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
+        "cpu_baseline": cpu,
+        "ops": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in ops.items()},
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
+        "fp8_over_bf16": ({k: (round(v, 3) if isinstance(v, float) else v) for k, v in ratio.items()}
+                          if ratio else None),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

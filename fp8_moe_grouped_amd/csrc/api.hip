@@ -1,0 +1,224 @@
+// C ABI of the library: argument validation, workspace layout and kernel
+// launches on the caller's stream.  Declarations and the contract of every
+// entry point are in include/fp8_moe_grouped.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/fp8_moe_grouped.h"
+#include "launch.hpp"
+
+using namespace fp8gmm;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int64_t M, int64_t K, int64_t N, int32_t G) {
+  if (M < 0 || M > kMaxRows || K <= 0 || N <= 0 || G <= 0) return FP8GMM_ERR_SHAPE;
+  if (G > kMaxGroups) return FP8GMM_ERR_UNSUPPORTED;
+  if (K % 128 != 0 || N % 128 != 0) return FP8GMM_ERR_UNSUPPORTED;
+  if ((long long)G * K * N >= (1LL << 40)) return FP8GMM_ERR_SHAPE;
+  return FP8GMM_OK;
+}
+
+// Forward workspace: activation codes [M, K] then row scales [M].
+size_t fwd_ws(int64_t M, int64_t K) { return align_up((size_t)M * K) + align_up((size_t)M * 4); }
+
+int fwd_common(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
+               int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale, void* ws,
+               size_t ws_bytes, int32_t* dev_status, void* stream, bool swiglu) {
+  if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!lhs || !out)) return FP8GMM_ERR_NULL;
+  if (K > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
+  if (swiglu && ((N / 2) % 128 != 0)) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(lhs) || !aligned16(codes) || !aligned16(scale) || !aligned16(out) ||
+      (dbg_codes && !aligned16(dbg_codes)))
+    return FP8GMM_ERR_ALIGN;   // NULL (M == 0) counts as aligned
+  const size_t need = fwd_ws(M, K);
+  if (M > 0 && (!ws || ws_bytes < need)) return FP8GMM_ERR_WORKSPACE;
+  if (M == 0) return FP8GMM_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* aq = dbg_codes ? dbg_codes : static_cast<uint8_t*>(ws);
+  float* as = dbg_scale ? dbg_scale : reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)M * K));
+  if (launch_quant_rows_e4m3(static_cast<const uint16_t*>(lhs), group_sizes, G, (int)M, (int)K, aq, as, s) !=
+      hipSuccess)
+    return FP8GMM_ERR_HIP;
+  if (launch_gmm_fp8_fwd(aq, as, codes, scale, group_sizes, G, (int)M, (int)K, (int)N, swiglu,
+                         static_cast<uint16_t*>(out), dev_status, s) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
+                int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale, void* ws,
+                size_t ws_bytes, int32_t* dev_status, void* stream) {
+  return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, dbg_codes, dbg_scale, ws, ws_bytes, dev_status,
+                    stream, false);
+}
+
+int gmm_silu_fp8(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
+                 int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale, void* ws,
+                 size_t ws_bytes, int32_t* dev_status, void* stream) {
+  return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, dbg_codes, dbg_scale, ws, ws_bytes, dev_status,
+                    stream, true);
+}
+
+int quantize_rows_fp8(const void* lhs, const int32_t* group_sizes, int64_t M, int64_t K, int32_t G,
+                      uint8_t* codes_out, float* scale_out, void* stream) {
+  if (!group_sizes) return FP8GMM_ERR_NULL;
+  if (M < 0 || M > kMaxRows || K <= 0 || G <= 0) return FP8GMM_ERR_SHAPE;
+  if (M > 0 && (!lhs || !codes_out || !scale_out)) return FP8GMM_ERR_NULL;
+  if (G > kMaxGroups || K % 128 != 0 || K > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(lhs) || !aligned16(codes_out)) return FP8GMM_ERR_ALIGN;
+  if (M == 0) return FP8GMM_OK;
+  if (launch_quant_rows_e4m3(static_cast<const uint16_t*>(lhs), group_sizes, G, (int)M, (int)K, codes_out, scale_out,
+                             reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+static int fwd_q_common(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
+                        const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
+                        int32_t* dev_status, void* stream, bool swiglu) {
+  if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!aq || !ascale || !out)) return FP8GMM_ERR_NULL;
+  if (swiglu && ((N / 2) % 128 != 0)) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(aq) || !aligned16(codes) || !aligned16(scale) || !aligned16(out)) return FP8GMM_ERR_ALIGN;
+  if (M == 0) return FP8GMM_OK;
+  if (launch_gmm_fp8_fwd(aq, ascale, codes, scale, group_sizes, G, (int)M, (int)K, (int)N, swiglu,
+                         static_cast<uint16_t*>(out), dev_status, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+int gmm_fp8_fwd_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
+                  const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
+                  int32_t* dev_status, void* stream) {
+  return fwd_q_common(aq, ascale, codes, scale, group_sizes, M, K, N, G, out, dev_status, stream, false);
+}
+
+int gmm_silu_fp8_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
+                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
+                   int32_t* dev_status, void* stream) {
+  return fwd_q_common(aq, ascale, codes, scale, group_sizes, M, K, N, G, out, dev_status, stream, true);
+}
+
+int dequantize_fp8_codes(const uint8_t* codes, const float* scale, int32_t G, int64_t K, int64_t N, void* out,
+                         void* stream) {
+  if (!codes || !scale || !out) return FP8GMM_ERR_NULL;
+  if (G <= 0 || K <= 0 || N <= 0) return FP8GMM_ERR_SHAPE;
+  if (N % 16 != 0) return FP8GMM_ERR_UNSUPPORTED;
+  if ((long long)G * K * N >= (1LL << 40)) return FP8GMM_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scale) || !aligned16(out)) return FP8GMM_ERR_ALIGN;
+  if (launch_dequant(codes, scale, G, K, N, static_cast<uint16_t*>(out), reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+int gmm_dlhs_fp8(const void* dout, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                 int64_t M, int64_t K, int64_t N, int32_t G, void* dlhs, void* ws, size_t ws_bytes,
+                 int32_t* dev_status, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!dout || !dlhs)) return FP8GMM_ERR_NULL;
+  if (!aligned16(dout) || !aligned16(codes) || !aligned16(scale) || !aligned16(dlhs)) return FP8GMM_ERR_ALIGN;
+  if (M == 0) return FP8GMM_OK;
+  if (launch_gmm_dlhs_fp8(static_cast<const uint16_t*>(dout), codes, scale, group_sizes, G, (int)M, (int)K, (int)N,
+                          static_cast<uint16_t*>(dlhs), dev_status, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+               int32_t G, int32_t grad_dtype, int32_t tile_m, float* drhs, float* dbg_sL, float* dbg_sD, void* ws,
+               size_t ws_bytes, int32_t* dev_status, void* stream) {
+  if (!group_sizes || !drhs) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!lhs || !dout)) return FP8GMM_ERR_NULL;
+  if (grad_dtype != FP8GMM_E4M3 && grad_dtype != FP8GMM_E5M2) return FP8GMM_ERR_UNSUPPORTED;
+  if (tile_m != 512 || K % 256 != 0) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(lhs) || !aligned16(dout) || !aligned16(drhs) || (dbg_sL && !aligned16(dbg_sL)) ||
+      (dbg_sD && !aligned16(dbg_sD)))
+    return FP8GMM_ERR_ALIGN;
+  const size_t need = tgmm_workspace_bytes(M, K, N, G);
+  if (need > 0 && (!ws || ws_bytes < need)) return FP8GMM_ERR_WORKSPACE;
+  if (launch_tgmm_quant(static_cast<const uint16_t*>(lhs), static_cast<const uint16_t*>(dout), group_sizes, G,
+                        (int)M, (int)K, (int)N, grad_dtype == FP8GMM_E5M2, drhs, dbg_sL, dbg_sD, ws, dev_status,
+                        reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+int gmm_bf16_fwd(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                 int32_t G, void* out, int32_t* dev_status, void* stream) {
+  if (!w || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!lhs || !out)) return FP8GMM_ERR_NULL;
+  if (!aligned16(lhs) || !aligned16(w) || !aligned16(out)) return FP8GMM_ERR_ALIGN;
+  if (M == 0) return FP8GMM_OK;
+  if (launch_gmm_bf16_fwd(static_cast<const uint16_t*>(lhs), static_cast<const uint16_t*>(w), group_sizes, G, (int)M,
+                          (int)K, (int)N, static_cast<uint16_t*>(out), dev_status,
+                          reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+int gmm_bf16_dlhs(const void* dout, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                  int32_t G, void* dlhs, int32_t* dev_status, void* stream) {
+  if (!w || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!dout || !dlhs)) return FP8GMM_ERR_NULL;
+  if (!aligned16(dout) || !aligned16(w) || !aligned16(dlhs)) return FP8GMM_ERR_ALIGN;
+  if (M == 0) return FP8GMM_OK;
+  if (launch_gmm_bf16_dlhs(static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(w), group_sizes, G,
+                           (int)M, (int)K, (int)N, static_cast<uint16_t*>(dlhs), dev_status,
+                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+size_t fp8gmm_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t G, int32_t tile_m) {
+  if (check_common(M, K, N, G) != FP8GMM_OK) return 0;
+  switch (op) {
+    case FP8GMM_OP_FWD:
+    case FP8GMM_OP_SILU:
+      return fwd_ws(M, K);
+    case FP8GMM_OP_TGMM:
+      return (tile_m == 512 && K % 256 == 0) ? tgmm_workspace_bytes(M, K, N, G) : 0;
+    default:
+      return 0;
+  }
+}
+
+const char* fp8gmm_status_string(int32_t status) {
+  switch (status) {
+    case FP8GMM_OK: return "ok";
+    case FP8GMM_ERR_NULL: return "a required pointer is NULL";
+    case FP8GMM_ERR_SHAPE: return "a size is out of range";
+    case FP8GMM_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case FP8GMM_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case FP8GMM_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8GMM_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Host-side launchers of the library's kernels (internal; the public C ABI is
+// include/fp8_moe_grouped.h).  Every launcher enqueues on `stream`, never
+// synchronises and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8gmm {
+
+// Largest K handled by the row quantizer (512 bf16 per lane-chunk x 32).
+constexpr int kMaxK = 16384;
+// Largest number of experts (the group table lives in LDS).
+constexpr int kMaxGroups = 1024;
+// Largest static row count (keeps the clamped row prefix sums in int32).
+constexpr long long kMaxRows = (1LL << 24) - 1;
+
+hipError_t launch_quant_rows_e4m3(const uint16_t* lhs, const int* group_sizes, int G, int M, int K,
+                                  uint8_t* codes, float* scales, hipStream_t stream);
+
+hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* wscale,
+                              const int* group_sizes, int G, int M, int K, int N, bool swiglu, uint16_t* out,
+                              int* status, hipStream_t stream);
+
+hipError_t launch_gmm_dlhs_fp8(const uint16_t* dout, const uint8_t* codes, const float* scale, const int* group_sizes,
+                               int G, int M, int K, int N, uint16_t* dlhs, int* status, hipStream_t stream);
+
+hipError_t launch_gmm_bf16_dlhs(const uint16_t* dout, const uint16_t* w, const int* group_sizes, int G, int M, int K,
+                                int N, uint16_t* dlhs, int* status, hipStream_t stream);
+
+hipError_t launch_gmm_bf16_fwd(const uint16_t* lhs, const uint16_t* w, const int* group_sizes, int G, int M, int K,
+                               int N, uint16_t* out, int* status, hipStream_t stream);
+
+// tgmm: workspace holds the transposed decoded operands and the scales.
+size_t tgmm_workspace_bytes(long long M, long long K, long long N, int G);
+hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const int* group_sizes, int G, int M, int K,
+                             int N, bool grad_e5m2, float* drhs, float* dbg_sl, float* dbg_sd, void* ws,
+                             int* status, hipStream_t stream);
+
+hipError_t launch_dequant(const uint8_t* codes, const float* scale, int G, long long K, long long N, uint16_t* out,
+                          hipStream_t stream);
+
+}  // namespace fp8gmm

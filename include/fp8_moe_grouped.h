@@ -1,0 +1,197 @@
+/*
+ * fp8_moe_grouped.h -- C ABI of the MI355X (gfx950) routed-expert FP8 grouped
+ * matmul library (libfp8_moe_grouped.so).
+ *
+ * The operations restate two pages:
+ *   [P1] "MoE: native FP8 QAT for routed-expert GMMs" (maxtext PR #5969)
+ *   [P3] "MoE fp8 backward: in-kernel drhs operand quantization + configurable
+ *        gradient dtype" (maxtext PR #4971)
+ *
+ * Common conventions
+ * ------------------
+ * - Every pointer argument except `stream`, `dev_status` and the debug outputs
+ *   is a device pointer to caller-owned memory.  The library never allocates,
+ *   frees or synchronises; each call only enqueues kernels on `stream`
+ *   (a hipStream_t; NULL is the null stream) and returns.
+ * - Tensors are row-major and contiguous with 16-byte aligned base pointers.
+ *   bf16 tensors are passed as `void*` holding IEEE bfloat16 bit patterns.
+ *   Inputs are never written and must not alias outputs or the workspace.
+ * - The static ragged buffer: lhs/dout have M rows.  Rows
+ *   [off_g, off_g + group_sizes[g]) belong to expert g, off_g = sum of the
+ *   sizes before g (P3, What: only the tiles covered by group_sizes are
+ *   touched).  Rows at or past sum(group_sizes) are stale: never read and,
+ *   in row outputs, never written.  `group_sizes` is an int32[G] device array;
+ *   a negative size counts as 0 and the running sum is clamped to M, so no
+ *   access leaves the buffer.  Such repairs OR bits into *dev_status (device
+ *   int32, may be NULL): FP8GMM_DEV_SUM_CLAMPED, FP8GMM_DEV_NEGATIVE_SIZE.
+ * - Weight codes are e4m3fn bytes [G, K, N] (N fastest) with one f32 scale
+ *   per (expert, output channel), scale[G, N] ([P1] Data flow table).
+ * - Pointers to buffers with M rows may be NULL when M == 0.
+ * - Host-checkable errors return before any HIP call; a failed launch returns
+ *   FP8GMM_ERR_HIP.  Outputs are then unspecified.
+ * - Shape limits: 0 <= M < 2^24, 1 <= G <= 1024, K and N multiples of 128,
+ *   K <= 16384 for ops that quantize activation rows.
+ */
+#ifndef FP8_MOE_GROUPED_H
+#define FP8_MOE_GROUPED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return status */
+#define FP8GMM_OK 0
+#define FP8GMM_ERR_NULL (-1)        /* a required pointer is NULL */
+#define FP8GMM_ERR_SHAPE (-2)       /* a size is out of range */
+#define FP8GMM_ERR_UNSUPPORTED (-3) /* a valid request this build does not implement */
+#define FP8GMM_ERR_ALIGN (-4)       /* a base pointer is not 16-byte aligned */
+#define FP8GMM_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than fp8gmm_workspace_bytes */
+#define FP8GMM_ERR_HIP (-6)         /* a kernel launch failed */
+
+/* bits of *dev_status */
+#define FP8GMM_DEV_SUM_CLAMPED 1    /* sum(group_sizes) > M, clamped */
+#define FP8GMM_DEV_NEGATIVE_SIZE 2  /* a negative size was treated as 0 */
+
+/* 8-bit formats of the tgmm gradient operand */
+#define FP8GMM_E4M3 0
+#define FP8GMM_E5M2 1
+
+/* op ids of fp8gmm_workspace_bytes */
+#define FP8GMM_OP_FWD 0
+#define FP8GMM_OP_SILU 1
+#define FP8GMM_OP_DLHS 2
+#define FP8GMM_OP_TGMM 3
+#define FP8GMM_OP_BF16_FWD 4
+#define FP8GMM_OP_BF16_DLHS 5
+
+/*
+ * gmm_fp8_fwd -- native FP8 forward GMM ([P1] Description: the forward GMMs
+ * run FP8 x FP8, read the codes and per-channel scale directly and quantize
+ * the activation inside the op; Implementation: one f32 scale per row over
+ * the full K, max(amax, 1e-12)/448, f32 accumulation).
+ *
+ *   s[r]    = f32( max(max_k |lhs[r,k]|, 1e-12) / 448 )
+ *   q[r,k]  = e4m3fn( f32(lhs[r,k] / s[r]) )   saturating, round to nearest even
+ *   out[r,n]= bf16( (sum_k q[r,k] * codes[g,k,n]) * s[r] * scale[g,n] )
+ *
+ * lhs        bf16 [M, K]
+ * codes      u8   [G, K, N]     e4m3fn weight codes
+ * scale      f32  [G, N]
+ * group_sizes i32 [G]
+ * out        bf16 [M, N]        rows >= sum(group_sizes) are not written
+ * dbg_codes  u8   [M, K] or NULL: receives q (the codes the GEMM consumes)
+ * dbg_scale  f32  [M] or NULL:    receives s
+ * ws         device workspace of ws_bytes >= fp8gmm_workspace_bytes(FP8GMM_OP_FWD, ...)
+ */
+int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                int64_t M, int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale,
+                void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * gmm_silu_fp8 -- gmm_fp8_fwd with a fused SwiGLU epilogue for wi ([P1]
+ * Implementation: gmm_silu_fp8).  The N = 2*I weight columns are [gate | up];
+ * with y the scaled f32 GEMM result of gmm_fp8_fwd (before rounding):
+ *   out[r,i] = bf16( silu(y[r,i]) * y[r,I+i] ),  silu(z) = z / (1 + exp(-z))
+ * out is bf16 [M, I].  I must be a multiple of 128.  Other arguments as above.
+ */
+int gmm_silu_fp8(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                 int64_t M, int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale,
+                 void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * The forward in two calls, for callers whose activations are already e4m3
+ * codes with one f32 scale per row (for example after an FP8 all-gather of
+ * tokens), or that time the two kernels separately.  gmm_fp8_fwd is exactly
+ * quantize_rows_fp8 followed by gmm_fp8_fwd_q (gmm_silu_fp8: gmm_silu_fp8_q).
+ *
+ * quantize_rows_fp8: for the valid rows r (r < sum(group_sizes), clamped),
+ *   scale_out[r] = s[r] and codes_out[r,:] = q[r,:] as defined for
+ *   gmm_fp8_fwd; other rows are not written.  lhs bf16 [M, K],
+ *   codes_out u8 [M, K], scale_out f32 [M].
+ * gmm_fp8_fwd_q / gmm_silu_fp8_q: the GEMM and epilogue of gmm_fp8_fwd /
+ *   gmm_silu_fp8 on activation codes aq u8 [M, K] and row scales ascale
+ *   f32 [M] (only valid rows are read).  No workspace.
+ */
+int quantize_rows_fp8(const void* lhs, const int32_t* group_sizes, int64_t M, int64_t K, int32_t G,
+                      uint8_t* codes_out, float* scale_out, void* stream);
+int gmm_fp8_fwd_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
+                  const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
+                  int32_t* dev_status, void* stream);
+int gmm_silu_fp8_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
+                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
+                   int32_t* dev_status, void* stream);
+
+/*
+ * gmm_dlhs_fp8 -- backward dLHS reading the FP8 codes ([P1] Description: the
+ * dLHS GMM reads the codes and dequantizes each tile on chip, no bf16 weight
+ * copy is written to HBM, bit-identical to the dequant path; Implementation:
+ * rhs_contract_dequant):
+ *   w[g,k,n]    = bf16( f32(codes[g,k,n] * scale[g,n]) )   (as dequantize_fp8_codes)
+ *   dlhs[r,k]   = bf16( sum_n dout[r,n] * w[g,k,n] )        f32 accumulation
+ * dout bf16 [M, N]; dlhs bf16 [M, K] (rows >= sum(group_sizes) not written).
+ * The call needs no workspace (ws may be NULL).
+ */
+int gmm_dlhs_fp8(const void* dout, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                 int64_t M, int64_t K, int64_t N, int32_t G, void* dlhs, void* ws, size_t ws_bytes,
+                 int32_t* dev_status, void* stream);
+
+/*
+ * tgmm_quant -- weight gradient with in-kernel operand quantization ([P3]
+ * What: moe_bwd_inkernel_quant quantizes the drhs operands per gm-tile and per
+ * channel, touching only rows covered by group_sizes; bwd_quantization_dtype
+ * selects e5m2 or e4m3 for the gradient).
+ * For each expert g and each buffer-aligned tile t (rows [t*tile_m,
+ * (t+1)*tile_m)) with T = rows(g) intersect tile non-empty:
+ *   sL[k] = f32(max(max_{r in T} |lhs[r,k]|, 1e-12) / 448)
+ *   sD[n] = f32(max(max_{r in T} |dout[r,n]|, 1e-12) / FMAX)   FMAX = 448 (e4m3) or 57344 (e5m2)
+ *   drhs[g,k,n] = f32( sum_t sL[k] sD[n] sum_{r in T} e4m3(lhs[r,k]/sL[k]) * grad(dout[r,n]/sD[n]) )
+ * Experts without rows get exact zeros.  drhs f32 [G, K, N] is written fully.
+ * lhs bf16 [M, K]; dout bf16 [M, N]; grad_dtype FP8GMM_E4M3 or FP8GMM_E5M2;
+ * tile_m must be 512 and K a multiple of 256.  dbg_sL f32 [Tn, K] / dbg_sD f32 [Tn, N] (or NULL)
+ * receive the scales of the Tn non-empty (expert, tile) pairs in (expert,
+ * tile) order; Tn <= ceil(M/tile_m) + G - 1.
+ */
+int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+               int32_t G, int32_t grad_dtype, int32_t tile_m, float* drhs, float* dbg_sL, float* dbg_sD, void* ws,
+               size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * dequantize_fp8_codes -- out[g,k,n] = bf16( f32(codes[g,k,n] * scale[g,n]) )
+ * ([P1] Implementation: dequantize_fp8_codes).  codes u8 [G, K, N],
+ * scale f32 [G, N], out bf16 [G, K, N].  N must be a multiple of 16.
+ */
+int dequantize_fp8_codes(const uint8_t* codes, const float* scale, int32_t G, int64_t K, int64_t N, void* out,
+                         void* stream);
+
+/*
+ * bf16 measurement arm: the same group schedule and MFMA main loops with bf16
+ * weights w[G, K, N] (for example the output of dequantize_fp8_codes) and no
+ * activation quantization.  It is the bf16 GMM the FP8 forward is compared
+ * against ([P1] Tests: kernel microbenchmark, the bf16 arm gets a weight
+ * dequantized beforehand), and gmm_bf16_dlhs(dout, dequantize_fp8_codes(codes,
+ * scale)) is bit-identical to gmm_dlhs_fp8(dout, codes, scale).
+ *   gmm_bf16_fwd : out[r,n]  = bf16( sum_k lhs[r,k] * w[g,k,n] ),  out bf16 [M, N]
+ *   gmm_bf16_dlhs: dlhs[r,k] = bf16( sum_n dout[r,n] * w[g,k,n] ), dlhs bf16 [M, K]
+ */
+int gmm_bf16_fwd(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                 int32_t G, void* out, int32_t* dev_status, void* stream);
+int gmm_bf16_dlhs(const void* dout, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                  int32_t G, void* dlhs, int32_t* dev_status, void* stream);
+
+/*
+ * fp8gmm_workspace_bytes -- device workspace the call `op` needs for these
+ * sizes (0 if none).  Returns 0 as well for sizes the op rejects.
+ */
+size_t fp8gmm_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t G, int32_t tile_m);
+
+/* fp8gmm_status_string -- static text of a status code. */
+const char* fp8gmm_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_MOE_GROUPED_H */

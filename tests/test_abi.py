@@ -1,0 +1,120 @@
+"""CPU tests of the C ABI boundary: the shared library loads, exports every
+function include/fp8_moe_grouped.h declares, and rejects bad arguments on the
+host before any HIP call (fake device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_moe_grouped_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(G.LIB_PATH):
+        pytest.skip("library not built")
+    return G.lib()
+
+
+def test_exports_every_declared_function():
+    L = _lib()
+    names = G.header_functions()
+    assert {"gmm_fp8_fwd", "gmm_silu_fp8", "gmm_dlhs_fp8", "tgmm_quant", "dequantize_fp8_codes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    # the binding's marshalling table covers the same entry points
+    for n in names:
+        if not n.startswith("fp8gmm_"):
+            assert n in G._SIGNATURES, n
+
+
+def test_header_macros_match_binding():
+    text = open(G.HEADER_PATH).read()
+    vals = {m: int(v) for m, v in re.findall(r"#define (FP8GMM_\w+) \(?(-?\d+)\)?", text)}
+    assert vals["FP8GMM_ERR_NULL"] == G.ERR_NULL and vals["FP8GMM_ERR_HIP"] == G.ERR_HIP
+    assert vals["FP8GMM_E4M3"] == G.E4M3 and vals["FP8GMM_E5M2"] == G.E5M2
+    assert vals["FP8GMM_OP_TGMM"] == G.OP_TGMM and vals["FP8GMM_DEV_NEGATIVE_SIZE"] == G.DEV_NEGATIVE_SIZE
+
+
+P = 0x10000          # fake, 16-byte aligned "device" address; never dereferenced
+BAD = 0x10008        # misaligned
+
+
+def _fwd(L, lhs=P, codes=P, scale=P, gs=P, M=256, K=128, N=256, Gn=4, out=P, ws=P, wsb=1 << 30, fn="gmm_fp8_fwd"):
+    return getattr(L, fn)(lhs, codes, scale, gs, M, K, N, Gn, out, None, None, ws, wsb, None, None)
+
+
+def test_forward_validation():
+    L = _lib()
+    for fn in ("gmm_fp8_fwd", "gmm_silu_fp8"):
+        assert _fwd(L, lhs=None, fn=fn) == G.ERR_NULL
+        assert _fwd(L, out=None, fn=fn) == G.ERR_NULL
+        assert _fwd(L, M=-1, fn=fn) == G.ERR_SHAPE
+        assert _fwd(L, M=1 << 24, fn=fn) == G.ERR_SHAPE
+        assert _fwd(L, K=0, fn=fn) == G.ERR_SHAPE
+        assert _fwd(L, Gn=0, fn=fn) == G.ERR_SHAPE
+        assert _fwd(L, K=100, fn=fn) == G.ERR_UNSUPPORTED
+        assert _fwd(L, N=200, fn=fn) == G.ERR_UNSUPPORTED
+        assert _fwd(L, K=16384 + 128, fn=fn) == G.ERR_UNSUPPORTED
+        assert _fwd(L, Gn=1025, fn=fn) == G.ERR_UNSUPPORTED
+        assert _fwd(L, lhs=BAD, fn=fn) == G.ERR_ALIGN
+        assert _fwd(L, ws=None, fn=fn) == G.ERR_WORKSPACE
+        need = L.fp8gmm_workspace_bytes(G.OP_FWD, 256, 128, 256, 4, 512)
+        assert need >= 256 * 128 + 256 * 4
+        assert _fwd(L, wsb=need - 1, fn=fn) == G.ERR_WORKSPACE
+        assert _fwd(L, M=0, ws=None, wsb=0, fn=fn) == G.OK          # empty buffer: a no-op
+    assert _fwd(L, N=384, fn="gmm_silu_fp8") == G.ERR_UNSUPPORTED   # I = 192 is not a multiple of 128
+
+
+def test_dlhs_and_tgmm_validation():
+    L = _lib()
+    assert L.gmm_dlhs_fp8(None, P, P, P, 8, 128, 128, 2, P, P, 1 << 20, None, None) == G.ERR_NULL
+    assert L.gmm_dlhs_fp8(P, P, P, P, -1, 128, 128, 2, P, P, 1 << 20, None, None) == G.ERR_SHAPE
+    assert L.gmm_dlhs_fp8(P, P, P, P, 8, 100, 128, 2, P, P, 1 << 20, None, None) == G.ERR_UNSUPPORTED
+    assert L.gmm_dlhs_fp8(P, P, P, P, 8, 128, 128, 2, BAD, P, 1 << 20, None, None) == G.ERR_ALIGN
+    args = lambda **kw: [kw.get("lhs", P), kw.get("dout", P), P, kw.get("M", 1024), 256, 128, 3,
+                         kw.get("gd", G.E5M2), kw.get("tm", 512), kw.get("drhs", P), None, None,
+                         kw.get("ws", P), kw.get("wsb", 1 << 30), None, None]
+    assert L.tgmm_quant(*args(lhs=None)) == G.ERR_NULL
+    assert L.tgmm_quant(*args(drhs=None)) == G.ERR_NULL
+    assert L.tgmm_quant(*args(gd=7)) == G.ERR_UNSUPPORTED
+    assert L.tgmm_quant(*args(tm=256)) == G.ERR_UNSUPPORTED
+    assert L.tgmm_quant(*args(M=-3)) == G.ERR_SHAPE
+    assert L.tgmm_quant(*args(dout=BAD)) == G.ERR_ALIGN
+    assert L.tgmm_quant(*args(ws=None)) == G.ERR_WORKSPACE
+
+
+def test_dequant_validation():
+    L = _lib()
+    assert L.dequantize_fp8_codes(None, P, 2, 128, 128, P, None) == G.ERR_NULL
+    assert L.dequantize_fp8_codes(P, P, 0, 128, 128, P, None) == G.ERR_SHAPE
+    assert L.dequantize_fp8_codes(P, P, 2, 128, 24, P, None) == G.ERR_UNSUPPORTED
+    assert L.dequantize_fp8_codes(P, P, 2, 128, 128, BAD, None) == G.ERR_ALIGN
+
+
+def test_workspace_and_status_strings():
+    L = _lib()
+    assert L.fp8gmm_workspace_bytes(G.OP_FWD, 256, 100, 256, 4, 512) == 0      # rejected sizes
+    assert L.fp8gmm_workspace_bytes(G.OP_SILU, 8192, 2048, 1536, 8, 512) >= 8192 * 2048
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert G.status_string(s) and G.status_string(s) != "unknown status"
+    assert G.status_string(-99) == "unknown status"
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    _lib()
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        G.gmm_fp8_fwd(x, torch.zeros((1, 128, 128), dtype=torch.uint8), torch.ones((1, 128)),
+                      torch.tensor([4], dtype=torch.int32))
+
+
+def test_product_path_does_not_import_oracle():
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "fp8_moe_grouped_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("no oracle", ""), os.path.join(dirpath, f)

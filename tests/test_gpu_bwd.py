@@ -1,0 +1,200 @@
+"""GPU parity of the backward ops (gmm_dlhs_fp8, tgmm_quant) and of the bf16
+measurement arm against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as F
+from oracle import gmm as O
+from tests.parity import bf16_np, check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+SENTINEL = 0x7FA1
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def sentinel(rows, cols):
+    return torch.full((rows, cols), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def run_dlhs(d, gs=None):
+    import fp8_moe_grouped_amd as G
+    gs = d["group_sizes"] if gs is None else gs
+    M, K = d["dout"].shape[0], d["codes"].shape[1]
+    out = sentinel(M, K)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    G.gmm_dlhs_fp8(dev(d["dout"]), dev(d["codes"]), dev(d["scale"]), dev(np.asarray(gs, np.int32)), out=out,
+                   dev_status=status)
+    torch.cuda.synchronize()
+    return out, int(status.item())
+
+
+def check_dlhs(d, rows=None, gs=None):
+    import fp8_moe_grouped_amd as G
+    gs = d["group_sizes"] if gs is None else gs
+    out, st = run_dlhs(d, gs)
+    got = bf16_np(out)
+    res = O.gmm_dlhs(d["dout"], d["codes"], d["scale"], gs, rows=rows)
+    N = d["dout"].shape[1]
+    err = check_bf16(got[res.rows], res.y, res.absum, res.group, N * 2.0 ** -24, "dlhs")
+    mv = O.layout(gs, d["dout"].shape[0]).valid
+    assert np.all(got[mv:] == SENTINEL), "rows past the valid prefix were written"
+    # bit-identity with the bf16 main loop fed by the standalone dequantization
+    w = G.dequantize_fp8_codes(dev(d["codes"]), dev(d["scale"]))
+    ref = sentinel(*out.shape)
+    G.gmm_bf16_dlhs(dev(d["dout"]), w, dev(np.asarray(gs, np.int32)), out=ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "dLHS tiles differ from dequantize_fp8_codes"
+    return err, st
+
+
+# ---------------------------------------------------------------- dLHS
+
+def test_dlhs_config2():
+    d = W.make(2, "dlhs_wo")
+    err, st = check_dlhs(d)
+    assert st == 0
+    print(f"config2 dlhs: normwise {err[0]:.2e} ratio {err[1]:.3f}")
+
+
+def test_dlhs_config0_shape():
+    d = W.make(0, "dlhs")             # K = 128: the narrow-tile path
+    err, _ = check_dlhs(d)
+    print(f"config0 dlhs: normwise {err[0]:.2e}")
+
+
+@pytest.mark.parametrize("op", ["dlhs_wi", "dlhs_wo"])
+def test_dlhs_config3_sampled(op):
+    d = W.make(3, op)
+    lay = O.layout(d["group_sizes"], d["M"])
+    r = np.random.default_rng(3)
+    rows = set(r.choice(lay.valid, 256, replace=False).tolist())
+    for g in range(len(d["group_sizes"])):
+        if lay.end[g] > lay.start[g]:
+            rows.update({int(lay.start[g]), int(lay.end[g]) - 1})
+    err, st = check_dlhs(d, rows=np.array(sorted(rows)))
+    assert st == 0
+    print(f"config3 {op}: normwise {err[0]:.2e} ratio {err[1]:.3f}")
+
+
+def test_dlhs_edges_and_stale_tail():
+    r = np.random.default_rng(4)
+    G_, M, K, N = 5, 200, 256, 384
+    codes = np.empty((G_, K, N), np.uint8)
+    scale = np.empty((G_, N), np.float32)
+    for g in range(G_):
+        codes[g], scale[g] = W.weight_codes(r.standard_normal((K, N)).astype(np.float32) * 0.02)
+    dout = W.to_bf16_bits(r.standard_normal((M, N)).astype(np.float32) * 1e-3)
+    base = dict(codes=codes, scale=scale, dout=dout)
+    gs = [0, 37, 1, 0, 90]
+    mv = sum(gs)
+    a = dict(base); a["dout"] = dout.copy(); a["dout"][mv:] = 0
+    b = dict(base); b["dout"] = dout.copy(); W.fill_garbage(b["dout"], mv)
+    check_dlhs(b, gs=gs)
+    oa, _ = run_dlhs(a, gs)
+    ob, _ = run_dlhs(b, gs)
+    assert torch.equal(oa[:mv].view(torch.int16), ob[:mv].view(torch.int16))
+    _, st = check_dlhs(base, gs=[150, -2, 100, 0, 0])
+    assert st == 3
+
+
+# ---------------------------------------------------------------- bf16 forward arm
+
+def test_bf16_forward_arm():
+    import fp8_moe_grouped_amd as G
+    d = W.make(2, "wo")
+    w = G.dequantize_fp8_codes(dev(d["codes"]), dev(d["scale"]))
+    out = sentinel(d["M"], d["N"])
+    G.gmm_bf16_fwd(dev(d["lhs"]), w, dev(d["group_sizes"]), out=out)
+    torch.cuda.synchronize()
+    got = bf16_np(out)
+    wd = F.bf16_to_f64(bf16_np(w))
+    x = F.bf16_to_f64(d["lhs"])
+    lay = O.layout(d["group_sizes"], d["M"])
+    for g in range(d["G"]):
+        a, b = lay.start[g], lay.end[g]
+        ref = x[a:b] @ wd[g]
+        absum = np.abs(x[a:b]) @ np.abs(wd[g])
+        check_bf16(got[a:b], ref, absum, np.zeros(b - a, int), d["K"] * 2.0 ** -24, "bf16 forward")
+
+
+# ---------------------------------------------------------------- tgmm
+
+def run_tgmm(lhs, dout, gs, grad, debug=True):
+    import fp8_moe_grouped_amd as G
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = G.tgmm_quant(dev(lhs), dev(dout), dev(np.asarray(gs, np.int32)), grad, 512, debug=debug,
+                       dev_status=status)
+    torch.cuda.synchronize()
+    return res, int(status.item())
+
+
+def _tgmm_small(seed, M=1500, K=256, N=128):
+    r = np.random.default_rng(seed)
+    lhs = W.to_bf16_bits(r.standard_normal((M, K)).astype(np.float32))
+    dout = W.to_bf16_bits(r.standard_normal((M, N)).astype(np.float32) * 1e-3)
+    return lhs, dout
+
+
+@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
+def test_tgmm_small_full(grad):
+    lhs, dout = _tgmm_small(5)
+    gs = [0, 300, 700, 0, 1, 400, 0]          # boundaries inside tiles, empty first/last experts
+    (drhs, sL, sD), st = run_tgmm(lhs, dout, gs, grad)
+    ref = O.tgmm_quant(lhs, dout, gs, grad, 512)
+    Tn = len(ref.tiles)
+    assert np.array_equal(sL.cpu().numpy()[:Tn], ref.sL) and np.array_equal(sD.cpu().numpy()[:Tn], ref.sD)
+    lay = O.layout(gs, lhs.shape[0])
+    tot, per = check_f32(drhs.cpu().numpy(), ref.drhs_f64, ref.absum, None,
+                         np.minimum(lay.end - lay.start, 512), f"tgmm {grad}")
+    assert np.all(drhs.cpu().numpy()[[0, 3, 6]] == 0)
+    print(f"tgmm small {grad}: rel fro {tot:.2e} (max per expert {per:.2e})")
+
+
+def test_tgmm_stale_tail_and_status():
+    lhs, dout = _tgmm_small(6, M=1300)
+    gs = [600, 0, 250]
+    mv = sum(gs)
+    la, da = lhs.copy(), dout.copy()
+    la[mv:] = 0; da[mv:] = 0
+    lb, db = lhs.copy(), dout.copy()
+    W.fill_garbage(lb, mv); W.fill_garbage(db, mv)
+    (a, _, _), _ = run_tgmm(la, da, gs, "e5m2")
+    (b, _, _), _ = run_tgmm(lb, db, gs, "e5m2")
+    assert torch.equal(a, b) and torch.isfinite(b).all()
+    _, st = run_tgmm(lhs, dout, [1000, -1, 500], "e4m3")
+    assert st == 3
+
+
+@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
+def test_tgmm_config4_sampled(grad):
+    d = W.make(4, "tgmm")
+    (drhs, sL, sD), st = run_tgmm(d["lhs"], d["dout"], d["group_sizes"], grad)
+    assert st == 0
+    r = np.random.default_rng(7)
+    kc = np.sort(r.choice(d["K"], 48, replace=False))
+    nc = np.sort(r.choice(d["N"], 48, replace=False))
+    ref = O.tgmm_quant(d["lhs"], d["dout"], d["group_sizes"], grad, 512, k_cols=kc, n_cols=nc)
+    got = drhs[:, torch.from_numpy(kc).cuda()][:, :, torch.from_numpy(nc).cuda()].cpu().numpy()
+    lay = O.layout(d["group_sizes"], d["M"])
+    tot, per = check_f32(got, ref.drhs_f64, ref.absum, None, np.minimum(lay.end - lay.start, 512), "tgmm cfg4")
+    Tn = len(ref.tiles)
+    assert np.array_equal(sL.cpu().numpy()[:Tn][:, kc], ref.sL)
+    assert np.array_equal(sD.cpu().numpy()[:Tn][:, nc], ref.sD)
+    # every channel's scale (not only the sampled ones), straight from the oracle's definition
+    for i, tl in enumerate(ref.tiles[:: max(1, Tn // 8)]):
+        j = ref.tiles.index(tl)
+        xl = F.bf16_to_f32(d["lhs"][tl.row0:tl.row1])
+        assert np.array_equal(sL.cpu().numpy()[j], O.column_scales(xl, 448.0))
+    empty = np.nonzero(np.asarray(d["group_sizes"]) == 0)[0]
+    for g in empty:
+        assert not torch.any(drhs[int(g)] != 0)
+    assert torch.isfinite(drhs).all()
+    print(f"tgmm config4 {grad}: rel fro {tot:.2e} (max per expert {per:.2e})")
