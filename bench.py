@@ -60,9 +60,12 @@ def make_inputs():
     gs = W.group_sizes(3)
     d = {"gs": gs, "G": G, "M": M, "valid": valid}
     d["codes_wi"], d["scale_wi"] = W.weights(3, W.W_WI, G, sh["K_wi"], sh["N_wi"])
+    log(f"[bench] wi weights {time.time() - t0:.1f}s")
     d["codes_wo"], d["scale_wo"] = W.weights(3, W.W_WO, G, sh["K_wo"], sh["N_wo"])
+    log(f"[bench] wo weights {time.time() - t0:.1f}s")
     d["lhs_wi"] = W.activations(3, W.LHS_WI, M, sh["K_wi"], valid, outlier_stream=W.OUTLIERS_WI)
     d["lhs_wo"] = W.activations(3, W.LHS_WO, M, sh["K_wo"], valid, outlier_stream=W.OUTLIERS_WO)
+    log(f"[bench] activations {time.time() - t0:.1f}s")
     d["dout_wi"] = W.gradients(3, W.DOUT_WI, M, sh["N_wi"], valid)
     d["dout_wo"] = W.gradients(3, W.DOUT_WO, M, sh["N_wo"], valid)
     t4 = W.make(4, "tgmm")
@@ -116,9 +119,9 @@ def cpu_baseline(d, seconds_target):
         t0 = time.time()
         O.gmm_fwd(d["lhs_wi"], d["codes_wi"], d["scale_wi"], d["gs"], swiglu_out=True, rows=rows)
         dt = time.time() - t0
-        if dt * 2 > seconds_target or n >= 4096:
+        if dt * 2 > seconds_target or n >= mv:
             break
-        n *= 2
+        n = min(2 * n, mv)
     fl = 2.0 * n * 7168 * 4096
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"wi forward + SwiGLU (K=7168, N=2x2048) of {n} of the {mv} valid rows, "

@@ -19,6 +19,7 @@ int check_common(int64_t M, int64_t K, int64_t N, int32_t G) {
   if (G > kMaxGroups) return FP8GMM_ERR_UNSUPPORTED;
   if (K % 128 != 0 || N % 128 != 0) return FP8GMM_ERR_UNSUPPORTED;
   if ((long long)G * K * N >= (1LL << 40)) return FP8GMM_ERR_SHAPE;
+  if ((long long)K * N >= (1LL << 31)) return FP8GMM_ERR_UNSUPPORTED;   // one expert's codes per buffer range
   return FP8GMM_OK;
 }
 

@@ -109,6 +109,30 @@ __device__ __forceinline__ v2i lds_read_tr8(const void* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(v2i, const_cast<void*>(p)));
 }
 
+// ----------------------------------------------------------------- global -> LDS copies
+
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+
+// Raw buffer resource over [base, base + bytes); loads at or past the end
+// return zeros instead of touching memory.
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte chunk per lane from buffer offset voff + soff straight into LDS:
+// lane i's chunk lands at lds_wave_base + 16*i (lds_wave_base is wave-uniform).
+__device__ __forceinline__ void dma16(BufRsrc r, void* lds_wave_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_wave_base), 16, voff, soff, 0, 0);
+}
+
+// Wait until every vector memory operation of this wave has completed
+// (s_waitcnt vmcnt(0); the other counters are left alone).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Scheduling fence: the compiler may not move instructions across it, so a
+// prefetch stays ahead of the MFMAs it is meant to overlap.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // ----------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -9,15 +9,24 @@
 //
 // Tiling (gfx950): a block owns a 256-row x BN-column output tile of one
 // expert, BN = 256 (or 128 when N is not a multiple of 256; for SwiGLU 128
-// gate + the matching 128 up columns), four waves own 128 x BN/2 each.  K advances 128 bytes per step through a double-buffered LDS
-// stage: the activation tile is stored row-major, the weight tile in its
-// natural [k][n] layout; both use a 16-byte-chunk XOR swizzle so the MFMA
-// operand reads are bank-conflict free.  The weight operand is read with the
-// transposing ds_read_tr8_b64, which hands each lane 8 consecutive k of one
-// column, so the N-contiguous codes need no transpose pass.  The MFMA is issued
-// with the weight as its first operand, which makes each lane own four
-// consecutive output columns of one row: the epilogue scales, optionally
-// applies SwiGLU, and stores 8-byte bf16 groups.
+// gate + the matching 128 up columns); four waves own 128 x BN/2 each, i.e.
+// 256 (or 128) f32 accumulators per lane held in AGPRs.  K advances 128 bytes
+// per step through two LDS stages:
+//  * both tiles are copied HBM/L2 -> LDS by buffer loads with the LDS
+//    destination (no VGPR staging), issued at the top of the step for the next
+//    stage; per-lane offsets are fixed, one scalar offset advances per step;
+//  * the activation tile is row-major, the weight tile keeps the natural
+//    [k][n] layout; 16-byte chunks are XOR-swizzled so that the operand reads
+//    hit distinct banks (gfx950 LDS serves 256 bytes per cycle);
+//  * the weight operand is read with the transposing ds_read_tr8_b64, which
+//    hands each lane 8 consecutive k of one column, so the N-contiguous codes
+//    need no transpose pass;
+//  * activation fragment f+1 is read while the 8 MFMAs of fragment f run, and
+//    after a mid-step barrier the next stage's weight fragments are read while
+//    the last two fragment groups run; scheduling fences keep this order.
+// The MFMA is issued with the weight as its first operand, which makes each
+// lane own four consecutive output columns of one row: the epilogue scales,
+// optionally applies SwiGLU, and stores 8-byte bf16 groups.
 //
 // Scheduling: every block rebuilds the expert table from group_sizes (a wave
 // scan), maps its id to a (global m-tile, n-tile) pair with an XCD-aware,
@@ -40,9 +49,15 @@ constexpr int stage_bytes() { return BM * BK + BK * BN; }
 template <int BN>
 constexpr int lds_main() { return 2 * stage_bytes<BN>(); }   // double buffered
 
-__device__ __forceinline__ int a_swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk swizzles (bank-conflict free operand reads on 64 banks).
+__device__ __forceinline__ int a_key(int row) { return (row >> 1) & 7; }
 template <int BN>
-__device__ __forceinline__ int b_swz(int kk, int chunk) { return kk * BN + ((chunk ^ (kk & 7)) << 4); }
+__device__ __forceinline__ int b_key(int kk) {
+  return BN == 256 ? ((kk & 7) | (((kk >> 5) & 1) << 3)) : (((kk >> 1) & 3) | (((kk >> 5) & 1) << 2));
+}
+__device__ __forceinline__ int a_swz(int row, int chunk) { return row * BK + ((chunk ^ a_key(row)) << 4); }
+template <int BN>
+__device__ __forceinline__ int b_swz(int kk, int chunk) { return kk * BN + ((chunk ^ b_key<BN>(kk)) << 4); }
 
 // NJ: 16-column MFMA fragments per wave along N (8 -> BN = 256, 4 -> BN = 128).
 template <bool SWIGLU, int NJ>
@@ -53,8 +68,9 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
                         uint16_t* __restrict__ out, int* status) {
   constexpr int BN = 32 * NJ;
   constexpr int kStageBytes = stage_bytes<BN>();
-  constexpr int kBChunksRow = BN / 16;                 // 16-byte chunks per weight-tile row
+  constexpr int kBChunksRow = BN / 16;                  // 16-byte chunks per weight-tile row
   constexpr int kBLoads = BK * kBChunksRow / kThreads;  // weight chunks per thread per stage
+  constexpr int kBRowsPerLoad = 1024 / BN;              // weight rows per wave-wide load
   static_assert(!SWIGLU || NJ == 8, "SwiGLU pairs 4 gate with 4 up fragments");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* t_start = reinterpret_cast<int*>(smem + lds_main<BN>());
@@ -64,7 +80,8 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   build_group_table(group_sizes, G, M, BM, GroupTable{t_start, t_end, t_pre}, status);
   __syncthreads();
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int I = N >> 1;
   const int n_tiles = SWIGLU ? (I / (BN / 2)) : (N / BN);
@@ -79,37 +96,33 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   const int first_m = (L / width) * kGroupM;
   const int gsz = min(T - first_m, kGroupM);
   const int mt = first_m + (L % width) % gsz;
-  const int nt = (L % width) / gsz;
-  const int g = find_group(t_pre, G, mt);
-  const int row0 = t_start[g] + (mt - t_pre[g]) * BM;
-  const int rows = min(BM, t_end[g] - row0);
+  // values read from the LDS table are wave-uniform: keep them in scalar registers
+  const int nt = __builtin_amdgcn_readfirstlane((L % width) / gsz);
+  const int g = __builtin_amdgcn_readfirstlane(find_group(t_pre, G, mt));
+  const int row0 = __builtin_amdgcn_readfirstlane(t_start[g] + (mt - t_pre[g]) * BM);
+  const int rows = __builtin_amdgcn_readfirstlane(min(BM, t_end[g] - row0));
 
-  const uint8_t* codes_g = codes + (size_t)g * K * N;
-
-  // ---- per-thread global source pointers (8 chunks of A and 8 of B per stage)
-  const uint8_t* pa[8];
-  int a_off[8];
+  // ---- buffer resources: the tile's activation rows and the expert's codes
+  const BufRsrc ra = make_rsrc(aq + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
+  const BufRsrc rb = make_rsrc(codes + (size_t)g * K * N, (uint32_t)K * (uint32_t)N);
+  uint32_t va[8];                      // activation chunk offsets (step 0)
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int i = tid + kThreads * j;
-    const int r = i >> 3, c = i & 7;
-    const int rr = row0 + min(r, rows - 1);
-    pa[j] = aq + (size_t)rr * K + (c << 4);
-    a_off[j] = a_swz(r, c);
+    const int r = 8 * (8 * wave + j) + (lane >> 3);
+    const int c = (lane & 7) ^ a_key(r);
+    va[j] = (uint32_t)min(r, rows - 1) * (uint32_t)K + (uint32_t)(c << 4);
   }
-  const uint8_t* pb[kBLoads];
-  int b_off[kBLoads];
+  uint32_t vb[kBLoads];                // weight chunk offsets (step 0)
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j) {
-    const int i = tid + kThreads * j;
-    const int kk = i / kBChunksRow, c = i % kBChunksRow;
+    const int kk = kBRowsPerLoad * (kBLoads * wave + j) + lane / kBChunksRow;
+    const int c = (lane % kBChunksRow) ^ b_key<BN>(kk);
     int col;
     if (SWIGLU) col = (c < 8) ? nt * (BN / 2) + (c << 4) : I + nt * (BN / 2) + ((c - 8) << 4);
     else col = nt * BN + (c << 4);
-    pb[j] = codes_g + (size_t)kk * N + col;
-    b_off[j] = b_swz<BN>(kk, c);
+    vb[j] = (uint32_t)kk * (uint32_t)N + (uint32_t)col;
   }
-  const size_t b_step = (size_t)BK * N;
+  const uint32_t b_step = (uint32_t)BK * (uint32_t)N;
 
   // ---- per-lane LDS read offsets of the MFMA operands
   int a_rd[8][2];
@@ -130,7 +143,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kk = (lane >> 4) * 32 + 8 * t + (Lg >> 1);
-      b_rd[j][t] = b_swz<BN>(kk, cb >> 4) + 8 * (Lg & 1);
+      b_rd[j][t] = BM * BK + b_swz<BN>(kk, cb >> 4) + 8 * (Lg & 1);
     }
   }
 
@@ -140,53 +153,65 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  v4i sa[8], sb[kBLoads];
   const int nk = K / BK;
-
-  auto load_stage = [&](int ks) {
+  auto issue_stage = [&](int ks, int buf) {
+    uint8_t* S = smem + buf * kStageBytes;
+    const uint32_t sa = (uint32_t)ks * BK, sb = (uint32_t)ks * b_step;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sa[j] = *reinterpret_cast<const v4i*>(pa[j] + (size_t)ks * BK);
+    for (int j = 0; j < 8; ++j) dma16(ra, S + (8 * wave + j) * 1024, va[j], sa);
 #pragma unroll
-    for (int j = 0; j < kBLoads; ++j) sb[j] = *reinterpret_cast<const v4i*>(pb[j] + (size_t)ks * b_step);
+    for (int j = 0; j < kBLoads; ++j) dma16(rb, S + BM * BK + (kBLoads * wave + j) * 1024, vb[j], sb);
   };
-  auto store_stage = [&](int buf) {
-    uint8_t* A = smem + buf * kStageBytes;
-    uint8_t* B = A + BM * BK;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<v4i*>(A + a_off[j]) = sa[j];
-#pragma unroll
-    for (int j = 0; j < kBLoads; ++j) *reinterpret_cast<v4i*>(B + b_off[j]) = sb[j];
+  auto read_a = [&](int buf, int f) {
+    const uint8_t* S = smem + buf * kStageBytes;
+    const v4i lo = *reinterpret_cast<const v4i*>(S + a_rd[f][0]);
+    const v4i hi = *reinterpret_cast<const v4i*>(S + a_rd[f][1]);
+    return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) load_stage(ks + 1);
-    const uint8_t* A = smem + buf * kStageBytes;
-    const uint8_t* B = A + BM * BK;
-    v8i bf[NJ];
+  auto read_b = [&](int buf, v8i* bf) {
+    const uint8_t* S = smem + buf * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const v2i v = lds_read_tr8(B + b_rd[j][t]);
+        const v2i v = lds_read_tr8(S + b_rd[j][t]);
         bf[j][2 * t] = v[0];
         bf[j][2 * t + 1] = v[1];
       }
-    }
+  };
+
+  // ---- prologue: stage 0 in LDS, its weight fragments and first activation fragment in registers
+  issue_stage(0, 0);
+  wait_vmem_all();
+  __syncthreads();
+  v8i bcur[NJ], bnxt[NJ];
+  read_b(0, bcur);
+  v8i acur = read_a(0, 0), anxt, a0n = acur;
+
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    const bool more = ks + 1 < nk;
+    if (more) issue_stage(ks + 1, buf ^ 1);
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      const v4i lo = *reinterpret_cast<const v4i*>(A + a_rd[f][0]);
-      const v4i hi = *reinterpret_cast<const v4i*>(A + a_rd[f][1]);
-      const v8i af = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (f < 7) anxt = read_a(buf, f + 1);
+      if (f == 6 && more) {
+        // every wave's copy of stage ks+1 has landed: fetch its first fragments
+        wait_vmem_all();
+        __syncthreads();
+        read_b(buf ^ 1, bnxt);
+        a0n = read_a(buf ^ 1, 0);
+      }
+      sched_fence();
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[f][j] = mfma_e4m3_16x16x128(bf[j], af, acc[f][j]);
+      for (int j = 0; j < NJ; ++j) acc[f][j] = mfma_e4m3_16x16x128(bcur[j], acur, acc[f][j]);
+      sched_fence();
+      if (f < 7) acur = anxt;
     }
-    if (ks + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bcur[j] = bnxt[j];
+    acur = a0n;
+    __syncthreads();   // stage ks fully consumed before it is refilled
   }
 
   // ---- epilogue: lane owns row (f*16 + lane%16) and columns cb(j) + 4*(lane/16) + 0..3

@@ -30,7 +30,7 @@
  * - Host-checkable errors return before any HIP call; a failed launch returns
  *   FP8GMM_ERR_HIP.  Outputs are then unspecified.
  * - Shape limits: 0 <= M < 2^24, 1 <= G <= 1024, K and N multiples of 128,
- *   K <= 16384 for ops that quantize activation rows.
+ *   K * N < 2^31, K <= 16384 for ops that quantize activation rows.
  */
 #ifndef FP8_MOE_GROUPED_H
 #define FP8_MOE_GROUPED_H
