@@ -39,6 +39,33 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 (OCP) MFMA
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes over this bench
+# (profiles/bench_dropless32_kernels.md), scaled by a plain 1 GiB copy: FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
+# were taken; once the sources change the figure no longer applies and traffic is null.
+MEASURED_TRAFFIC_MIB = {
+    "wi_gemm": ("gmm_fwd.hip", "c45e9372b952b201", 1811, 78),
+    "wo_gemm": ("gmm_fwd.hip", "c45e9372b952b201", 830, 269),
+    "wi_dlhs": ("dlhs.hip", "c4e03a62b25700e7", 2326, 308),
+    "wo_dlhs": ("dlhs.hip", "c4e03a62b25700e7", 1309, 88),
+    "tgmm": ("tgmm.hip", "f63dced80ce36c0b", 346 + 1836, 374 + 1934),
+    "dequant": ("dequant.hip", "d010579fd4be2bf7", 455, 1083),
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` if its sources are those the counters were taken on."""
+    import hashlib
+    if kernel not in MEASURED_TRAFFIC_MIB:
+        return None
+    src, digest, rd, wr = MEASURED_TRAFFIC_MIB[kernel]
+    csrc = os.path.join(ROOT, "fp8_moe_grouped_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (src, "common.hpp", "launch.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return (rd + wr) * 2 ** 20 if h.hexdigest()[:16] == digest else None
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -136,6 +163,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-arm", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy (read MIB, write MIB) three times; used to scale "
+                         "the FETCH_SIZE / WRITE_SIZE hardware counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
@@ -145,6 +175,17 @@ def main():
     import fp8_moe_grouped_amd as G
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     G.lib()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 18                     # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 3}}))
+        return
 
     d = make_inputs()
     gs = to_dev(d["gs"])
@@ -247,7 +288,8 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": by[dom] / (op_ms[dom] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
+    roof["traffic_unit"] = "HBM bytes per launch"
 
     # bf16 arm: same scheduler, weights dequantized beforehand (not timed)
     ratio = None
