@@ -34,11 +34,12 @@ constexpr float kAmaxFloor = 1e-12f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Round-to-nearest-even f32 -> bf16 bits (hardware conversion, gfx950).
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even f32 -> bf16 bits, two at a time (one packed
+// hardware conversion on gfx950; lo lands in bits 0..15).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(((v2f){lo, hi}), v2bf));
 }
 
 // ----------------------------------------------------------------- fp8
@@ -129,9 +130,39 @@ __device__ __forceinline__ void dma16(BufRsrc r, void* lds_wave_base, uint32_t v
 // (s_waitcnt vmcnt(0); the other counters are left alone).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One dword per lane: lane i's value lands at lds_wave_base + 4*i.
+__device__ __forceinline__ void dma4(BufRsrc r, void* lds_wave_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_wave_base), 4, voff, soff, 0, 0);
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding
+// (they complete in issue order, so the older ones have landed) and every LDS
+// operation has completed: s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N>
+__device__ __forceinline__ void wait_vmem_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+  asm volatile("" ::: "memory");   // no load of the landed data may be hoisted above the wait
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): it does not
+// wait for this wave's outstanding LDS-destination loads, which is what lets
+// a copy two stages ahead stay in flight.  Callers wait for what they need
+// (wait_vmem_lds) before it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Scheduling fence: the compiler may not move instructions across it, so a
 // prefetch stays ahead of the MFMAs it is meant to overlap.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Ask the scheduler for a group of `n` instructions of the classes in `mask`
+// (0x2 VALU, 0x8 MFMA, 0x100 LDS read, 0x20 VMEM read) at this point of the
+// sequence; consecutive calls with the same id interleave the classes.
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // ----------------------------------------------------------------- reductions
 

@@ -9,39 +9,79 @@
 // w[g, k, n] = bf16( f32(dec(codes[g, k, n]) * scale[g, n]) ).
 //
 // The scale runs along the contraction axis n, so it cannot move to the
-// epilogue: each stage's [BN x 64] code tile is loaded from HBM, dequantized
-// once per block (exact e4m3 decode, one f32 multiply, round-to-nearest-even
-// bf16 -- the arithmetic of dequantize_fp8_codes) and written to LDS as bf16,
-// where four waves read it as bf16 MFMA operands.  The same main loop also
-// runs with bf16 weights (FROM_CODES = false), which is the bf16 measurement
-// arm; fed with dequantize_fp8_codes' output it must reproduce the FP8-code
-// result bit for bit, which proves the on-chip tiles equal the standalone
-// dequantization.
+// epilogue: every weight element is decoded exactly, multiplied by its f32
+// scale and rounded to bf16 (the arithmetic of dequantize_fp8_codes) before
+// it enters a bf16 MFMA with f32 accumulation.
 //
-// Tiling: 256 rows x BN output columns per block (BN = 256 or 128), four
-// waves of 128 x BN/2, contraction 64 per stage (two 16x16x32 bf16 MFMA
-// steps).  Both LDS tiles are [rows][64 bf16] with a 16-byte-chunk XOR
-// swizzle.  The MFMA takes the weight as its first operand so each lane owns
-// four consecutive output columns of one row.  Group scheduling and the
-// never-read / never-written stale rows are as in the forward.
+// Tiling (gfx950): a block owns 256 rows x BN output columns of one expert
+// (BN = 256, or 128 when K is not a multiple of 256); four waves own
+// 128 x BN/2 each (256 or 128 f32 accumulators per lane, in AGPRs).  The
+// contraction advances 64 per stage through a ring of LDS stages (three for
+// FP8 codes, two for bf16 weights), each holding
+//   * the dout tile, [256 rows][64 bf16], 16-byte chunks XOR-swizzled;
+//   * the weight tile in its natural [k][n] layout (n contiguous, which is the
+//     contraction), [BN rows][64 codes] or [BN rows][64 bf16], swizzled;
+//   * per wave, the 64 scales of the stage.
+// Every byte reaches LDS through buffer loads with an LDS destination,
+// issued two stages ahead (codes) so HBM latency hides behind two stages of
+// MFMAs; one barrier per stage, placed before the next stage is first read.
+//
+// Inner loop: the wave keeps its 128-row dout operand of the stage in
+// registers and streams the weight fragments (16 output columns each): the
+// fragment two ahead is read from LDS, the fragment one ahead is decoded and
+// rounded on the VALU between the 16 MFMAs of the current one.  Each lane
+// reads 16 consecutive contraction values of a row, which the two 16x16x32
+// MFMAs of a stage take as their two 8-value halves; dout and the weight use
+// the same assignment, so the order of summation is the same whether the
+// weights arrive as codes or as bf16 (the bf16 path is the measurement arm
+// and, fed with dequantize_fp8_codes' output, must reproduce the FP8-code
+// result bit for bit).  The MFMA takes the weight as its first operand so
+// each lane owns four consecutive output columns of one row.  Group
+// scheduling and the never-read / never-written stale rows are as in the
+// forward.
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace fp8gmm {
 namespace {
 
 constexpr int BM = 256;
-constexpr int BKN = 64;                 // contraction (n) per stage, bf16 elements
-constexpr int kRowBytes = BKN * 2;      // 128 bytes per LDS tile row
+constexpr int BKN = 64;                 // contraction (n) per stage
+constexpr int kARow = BKN * 2;          // 128 bytes per dout tile row
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 
-template <int BN>
-constexpr int stage_bytes() { return (BM + BN) * kRowBytes; }
-template <int BN>
-constexpr int lds_main() { return 2 * stage_bytes<BN>(); }
+template <bool FROM_CODES, int NJ>
+struct Cfg {
+  static constexpr int BN = 32 * NJ;                         // output columns per block
+  static constexpr int kWRow = FROM_CODES ? BKN : BKN * 2;   // bytes per weight tile row
+  static constexpr int kABytes = BM * kARow;
+  static constexpr int kWBytes = BN * kWRow;
+  static constexpr int kSBytes = FROM_CODES ? 4 * 256 : 0;   // one copy of the 64 scales per wave
+  static constexpr int kStage = kABytes + kWBytes + kSBytes;
+  static constexpr int kStages = FROM_CODES ? 3 : 2;
+  static constexpr int kLds = kStages * kStage;
+  static constexpr int kWLoads = kWBytes / (4 * 1024);        // 1 KB wave-wide loads per wave per stage
+  static constexpr int kLoads = 8 + kWLoads + (FROM_CODES ? 1 : 0);
+  static_assert(kLoads < 64, "outstanding loads fit vmcnt");
+};
 
-__device__ __forceinline__ int t_swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk swizzles, conflict-free for the operand reads (16 lanes read
+// 16 consecutive rows at one logical chunk).
+__device__ __forceinline__ int a_swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+__device__ __forceinline__ int w_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ v8bf as_bf(const v4i& v) { return __builtin_bit_cast(v8bf, v); }
+
+// 8 codes (two dwords, n = 0..7 of sc) -> 8 bf16 weights.
+__device__ __forceinline__ v4i deq8(uint32_t w0, uint32_t w1, const float* sc) {
+  const v2f a = dec_e4m3x2<false>(w0), b = dec_e4m3x2<true>(w0);
+  const v2f c = dec_e4m3x2<false>(w1), d = dec_e4m3x2<true>(w1);
+  return (v4i){(int)pack_bf16x2(a[0] * sc[0], a[1] * sc[1]), (int)pack_bf16x2(b[0] * sc[2], b[1] * sc[3]),
+               (int)pack_bf16x2(c[0] * sc[4], c[1] * sc[5]), (int)pack_bf16x2(d[0] * sc[6], d[1] * sc[7])};
+}
 
 template <bool FROM_CODES, int NJ>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
@@ -49,20 +89,19 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
                      const float* __restrict__ wscale, const uint16_t* __restrict__ wbf16,
                      const int* __restrict__ group_sizes, int G, int M, int K, int N,
                      uint16_t* __restrict__ dlhs, int* status) {
-  constexpr int BN = 32 * NJ;
-  constexpr int kStage = stage_bytes<BN>();
-  // weight chunks per thread per stage: 16 codes (FROM_CODES) or 8 bf16 per chunk
-  constexpr int kWChunksRow = FROM_CODES ? BKN / 16 : BKN / 8;
-  constexpr int kWLoads = BN * kWChunksRow / kThreads;
+  using C = Cfg<FROM_CODES, NJ>;
+  constexpr int BN = C::BN;
+  constexpr int S = C::kStages;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int* t_start = reinterpret_cast<int*>(smem + lds_main<BN>());
+  int* t_start = reinterpret_cast<int*>(smem + C::kLds);
   int* t_end = t_start + G;
   int* t_pre = t_end + G;
 
   build_group_table(group_sizes, G, M, BM, GroupTable{t_start, t_end, t_pre}, status);
   __syncthreads();
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int n_tiles = K / BN;
   const int T = t_pre[G];
@@ -75,53 +114,98 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   const int first_m = (L / width) * kGroupM;
   const int gsz = min(T - first_m, kGroupM);
   const int mt = first_m + (L % width) % gsz;
-  const int nt = (L % width) / gsz;
-  const int g = find_group(t_pre, G, mt);
-  const int row0 = t_start[g] + (mt - t_pre[g]) * BM;
-  const int rows = min(BM, t_end[g] - row0);
+  // values read from the LDS table are wave-uniform: keep them in scalar registers
+  const int nt = __builtin_amdgcn_readfirstlane((L % width) / gsz);
+  const int g = __builtin_amdgcn_readfirstlane(find_group(t_pre, G, mt));
+  const int row0 = __builtin_amdgcn_readfirstlane(t_start[g] + (mt - t_pre[g]) * BM);
+  const int rows = __builtin_amdgcn_readfirstlane(min(BM, t_end[g] - row0));
 
-  // ---- activation-gradient (dout) loads: 8 x 16 bytes per thread per stage
-  const uint16_t* pa[8];
-  int a_off[8];
+  // ---- buffer resources and per-lane copy offsets (stage 0)
+  const BufRsrc ra = make_rsrc(dout + (size_t)row0 * N, (uint32_t)rows * (uint32_t)N * 2u);
+  const BufRsrc rw = FROM_CODES ? make_rsrc(codes + (size_t)g * K * N, (uint32_t)K * (uint32_t)N)
+                                : make_rsrc(wbf16 + (size_t)g * K * N, (uint32_t)K * (uint32_t)N * 2u);
+  const BufRsrc rs = make_rsrc(FROM_CODES ? wscale + (size_t)g * N : wscale, FROM_CODES ? (uint32_t)N * 4u : 0u);
+  uint32_t va[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int i = tid + kThreads * j;
-    const int r = i >> 3, c = i & 7;
-    const int rr = row0 + min(r, rows - 1);
-    pa[j] = dout + (size_t)rr * N + c * 8;
-    a_off[j] = t_swz(r, c);
+    const int r = 8 * (8 * wave + j) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    va[j] = (uint32_t)min(r, rows - 1) * (uint32_t)N * 2u + (uint32_t)(c << 4);
   }
-  // ---- weight loads
-  const size_t wrow0 = (size_t)g * K + (size_t)nt * BN;
-  const uint8_t* pw8[kWLoads];
-  const uint16_t* pw16[kWLoads];
-  int w_off[kWLoads];
-  int wc = 0;
+  uint32_t vw[C::kWLoads];
 #pragma unroll
-  for (int j = 0; j < kWLoads; ++j) {
-    const int i = tid + kThreads * j;
-    const int kk = i / kWChunksRow, c = i % kWChunksRow;
-    wc = c;
+  for (int j = 0; j < C::kWLoads; ++j) {
     if (FROM_CODES) {
-      pw8[j] = codes + (wrow0 + kk) * N + c * 16;
-      w_off[j] = t_swz(kk, 2 * c);          // 16 codes -> two 16-byte bf16 chunks
+      const int kr = 16 * (C::kWLoads * wave + j) + (lane >> 2);
+      const int c = (lane & 3) ^ ((kr >> 2) & 3);
+      vw[j] = (uint32_t)(nt * BN + kr) * (uint32_t)N + (uint32_t)(c << 4);
     } else {
-      pw16[j] = wbf16 + (wrow0 + kk) * N + c * 8;
-      w_off[j] = t_swz(kk, c);
+      const int kr = 8 * (C::kWLoads * wave + j) + (lane >> 3);
+      const int c = (lane & 7) ^ ((kr >> 1) & 7);
+      vw[j] = (uint32_t)(nt * BN + kr) * (uint32_t)N * 2u + (uint32_t)(c << 4);
     }
   }
-  const float* psc = wscale + (size_t)g * N + wc * 16;   // FROM_CODES: same 16 scales for all chunks
 
-  // ---- MFMA operand read offsets (16x16x32 bf16: lane row l%16, 8 contraction values)
-  int a_rd[8][2], b_rd[NJ][2];
+  // ---- per-lane LDS read offsets (within a stage)
+  const int q = lane >> 4;
+  int a_rd[2];
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int s = 0; s < 2; ++s) a_rd[s] = a_swz(wm * 128 + (lane & 15), 2 * q + s);   // + f * 2048
+  int w_rd[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) a_rd[f][s] = t_swz(wm * 128 + f * 16 + (lane & 15), s * 4 + (lane >> 4));
+  for (int s = 0; s < 2; ++s)
+    w_rd[s] = C::kABytes + (FROM_CODES ? w_swz(wn * (16 * NJ) + (lane & 15), q)           // + j * 1024
+                                       : a_swz(wn * (16 * NJ) + (lane & 15), 2 * q + s));  // + j * 2048
+  const int s_rd = C::kABytes + C::kWBytes + wave * 256 + q * 64;
+
+  auto issue_stage = [&](int ks) {
+    uint8_t* St = smem + (ks % S) * C::kStage;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < 8; ++j) dma16(ra, St + (8 * wave + j) * 1024, va[j], (uint32_t)ks * kARow);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) b_rd[j][s] = t_swz(wn * (16 * NJ) + j * 16 + (lane & 15), s * 4 + (lane >> 4));
+    for (int j = 0; j < C::kWLoads; ++j)
+      dma16(rw, St + C::kABytes + (C::kWLoads * wave + j) * 1024, vw[j], (uint32_t)ks * C::kWRow);
+    if (FROM_CODES) dma4(rs, St + C::kABytes + C::kWBytes + wave * 256, (uint32_t)lane * 4u, (uint32_t)ks * 256u);
+  };
+  // weight fragment j of stage ks, as read from LDS (codes: 16 bytes; bf16: 2 x 16 bytes)
+  auto read_w = [&](int ks, int j) {
+    const uint8_t* St = smem + (ks % S) * C::kStage;
+    v8i r;
+    if (FROM_CODES) {
+      const v4i v = *reinterpret_cast<const v4i*>(St + w_rd[0] + j * 1024);
+      r = (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    } else {
+      const v4i lo = *reinterpret_cast<const v4i*>(St + w_rd[0] + j * 2048);
+      const v4i hi = *reinterpret_cast<const v4i*>(St + w_rd[1] + j * 2048);
+      r = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    return r;
+  };
+  auto read_scales = [&](int ks, float* sc) {
+    const uint8_t* St = smem + (ks % S) * C::kStage;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v4f v = *reinterpret_cast<const v4f*>(St + s_rd + 16 * t);
+      sc[4 * t] = v[0]; sc[4 * t + 1] = v[1]; sc[4 * t + 2] = v[2]; sc[4 * t + 3] = v[3];
+    }
+  };
+  auto read_a = [&](int ks, v4i (*a)[2]) {
+    const uint8_t* St = smem + (ks % S) * C::kStage;
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(St + a_rd[s] + f * 2048);
+  };
+  // raw fragment -> the two MFMA operands (halves n = 0..7 and 8..15 of the lane's 16)
+  auto convert = [&](const v8i& r, const float* sc, v4i* w) {
+    if (FROM_CODES) {
+      w[0] = deq8((uint32_t)r[0], (uint32_t)r[1], sc);
+      w[1] = deq8((uint32_t)r[2], (uint32_t)r[3], sc + 8);
+    } else {
+      w[0] = (v4i){r[0], r[1], r[2], r[3]};
+      w[1] = (v4i){r[4], r[5], r[6], r[7]};
+    }
+  };
 
   v4f acc[8][NJ];
 #pragma unroll
@@ -129,83 +213,85 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  v4i sa[8], sw[kWLoads];
-  v4f ssc[4];
   const int nk = N / BKN;
 
-  auto load_stage = [&](int ks) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sa[j] = *reinterpret_cast<const v4i*>(pa[j] + (size_t)ks * BKN);
-    if (FROM_CODES) {
-#pragma unroll
-      for (int j = 0; j < kWLoads; ++j) sw[j] = *reinterpret_cast<const v4i*>(pw8[j] + (size_t)ks * BKN);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ssc[q] = *reinterpret_cast<const v4f*>(psc + (size_t)ks * BKN + 4 * q);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kWLoads; ++j) sw[j] = *reinterpret_cast<const v4i*>(pw16[j] + (size_t)ks * BKN);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t* A = smem + buf * kStage;
-    uint8_t* B = A + BM * kRowBytes;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<v4i*>(A + a_off[j]) = sa[j];
-#pragma unroll
-    for (int j = 0; j < kWLoads; ++j) {
-      if (FROM_CODES) {
-        // dequantize 16 codes: exact decode, f32 product, RNE to bf16
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w = (uint32_t)sw[j][q];
-          const v2f lo = dec_e4m3x2<false>(w);
-          const v2f hi = dec_e4m3x2<true>(w);
-          o[2 * q] = pack_bf16x2(lo[0] * ssc[q][0], lo[1] * ssc[q][1]);
-          o[2 * q + 1] = pack_bf16x2(hi[0] * ssc[q][2], hi[1] * ssc[q][3]);
-        }
-        *reinterpret_cast<v4i*>(B + w_off[j]) = (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-        // second 8 values go to the next logical chunk of the same row
-        const int kk = (tid + kThreads * j) / kWChunksRow;
-        const int c2 = 2 * ((tid + kThreads * j) % kWChunksRow) + 1;
-        *reinterpret_cast<v4i*>(B + t_swz(kk, c2)) = (v4i){(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
-      } else {
-        *reinterpret_cast<v4i*>(B + w_off[j]) = sw[j];
-      }
-    }
-  };
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) load_stage(ks + 1);
-    const uint8_t* A = smem + buf * kStage;
-    const uint8_t* B = A + BM * kRowBytes;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8bf bfr[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[j] = *reinterpret_cast<const v8bf*>(B + b_rd[j][s]);
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const v8bf af = *reinterpret_cast<const v8bf*>(A + a_rd[f][s]);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[f][j] = mfma_bf16_16x16x32(bfr[j], af, acc[f][j]);
-      }
-    }
-    if (ks + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
+  // ---- prologue: stages 0 .. S-2 in flight, stage 0 landed and its operands in registers
+  issue_stage(0);
+  if (S == 3 && nk > 1) {
+    issue_stage(1);
+    wait_vmem_lds<C::kLoads>();
+  } else {
+    wait_vmem_lds<0>();
   }
+  barrier_only();
+  v4i a[8][2];
+  read_a(0, a);
+  float sc[16], scn[16];
+  if (FROM_CODES) read_scales(0, sc);
+  v4i wcur[2];
+  v8i rawn = read_w(0, 1);
+  convert(read_w(0, 0), sc, wcur);
+
+  // One stage.  ISSUE: start the copy of stage ks+S-1; MORE: stage ks+1 exists
+  // (its operands are fetched during the last two weight fragments).
+  auto step = [&](int ks, auto issue_c, auto more_c) {
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr bool MORE = decltype(more_c)::value;
+    if (ISSUE) issue_stage(ks + S - 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      v8i raw2 = rawn;
+      if (MORE && j == NJ - 2) {
+        // every wave's copy of stage ks+1 has landed (stage ks+2 may still be in flight)
+        if (S == 3 && ISSUE) wait_vmem_lds<C::kLoads>();
+        else wait_vmem_lds<0>();
+        barrier_only();
+        if (FROM_CODES) read_scales(ks + 1, scn);
+      }
+      if (j + 2 < NJ) raw2 = read_w(ks, j + 2);
+      else if (MORE) raw2 = read_w(ks + 1, j + 2 - NJ);
+      sched_fence();
+      v4i wnext[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          acc[f][j] = mfma_bf16_16x16x32(as_bf(wcur[s]), as_bf(a[f][s]), acc[f][j]);
+          // last fragment of the stage: a[f][s] is free, refill it from stage ks+1
+          if (MORE && j == NJ - 1) a[f][s] = *reinterpret_cast<const v4i*>(smem + ((ks + 1) % S) * C::kStage +
+                                                                            a_rd[s] + f * 2048);
+        }
+      if (j + 1 < NJ || MORE) convert(rawn, (j == NJ - 1) ? scn : sc, wnext);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        SCHED_GROUP(0x008, 1);
+        SCHED_GROUP(0x002, 2);
+        if (MORE && j == NJ - 1) SCHED_GROUP(0x100, 1);
+      }
+      sched_fence();
+      wcur[0] = wnext[0];
+      wcur[1] = wnext[1];
+      rawn = raw2;
+    }
+    if (FROM_CODES && MORE) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = scn[i];
+    }
+  };
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int ks = 0;
+  for (; ks + S - 1 < nk; ++ks) step(ks, T_{}, T_{});      // steady state: copy S-1 ahead
+  if (S == 3 && ks + 1 < nk) step(ks++, F_{}, T_{});       // second to last (three stages)
+  step(ks, F_{}, F_{});                                    // last
 
   // ---- epilogue: lane owns row f*16 + lane%16, columns cb(j) + 4*(lane/16) + 0..3
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int ml = wm * 128 + f * 16 + (lane & 15);
     if (ml < rows) {
-      uint16_t* orow = dlhs + (size_t)(row0 + ml) * K + nt * BN + wn * (16 * NJ) + 4 * (lane >> 4);
+      uint16_t* orow = dlhs + (size_t)(row0 + ml) * K + nt * BN + wn * (16 * NJ) + 4 * q;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         v2i pk;
@@ -226,12 +312,12 @@ hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const fl
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
   if (K % 256 == 0) {
     hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 8>), dim3((unsigned)(max_m_tiles * (K / 256))), dim3(kThreads),
-                       lds_main<256>() + table, stream, dout, codes, scale, wbf16, group_sizes, G, M, K, N, dlhs,
-                       status);
+                       (Cfg<FROM_CODES, 8>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K, N,
+                       dlhs, status);
   } else {
     hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 4>), dim3((unsigned)(max_m_tiles * (K / 128))), dim3(kThreads),
-                       lds_main<128>() + table, stream, dout, codes, scale, wbf16, group_sizes, G, M, K, N, dlhs,
-                       status);
+                       (Cfg<FROM_CODES, 4>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K, N,
+                       dlhs, status);
   }
   return hipGetLastError();
 }
