@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp8gmm {
 
 // Largest K handled by the row quantizer (512 bf16 per lane-chunk x 32).
@@ -14,6 +16,22 @@ constexpr int kMaxK = 16384;
 constexpr int kMaxGroups = 1024;
 // Largest static row count (keeps the clamped row prefix sums in int32).
 constexpr long long kMaxRows = (1LL << 24) - 1;
+
+// Compute units of the current device, looked up once per device id
+// (persistent kernels launch one block per CU).
+inline int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 hipError_t launch_quant_rows_e4m3(const uint16_t* lhs, const int* group_sizes, int G, int M, int K,
                                   uint8_t* codes, float* scales, hipStream_t stream);

@@ -13,19 +13,30 @@
 // Two kernels:
 //  1. prep: one block per (pair, 64-column chunk of lhs or dout) reads only
 //     the pair's valid rows once, reduces the column amax (wave shuffles +
-//     LDS), writes the scales, quantizes, and stores the exactly decoded
-//     8-bit values as bf16 transposed ([column][row], row-padded with zeros to
-//     a multiple of 64) into the workspace.
-//  2. gemm: one block per (expert, 256-row k tile, 128-column n tile) walks
-//     the expert's pairs; the contraction over rows runs on bf16 MFMA (every
-//     e4m3/e5m2 value is exact in bf16 and products are exact in f32), so the
-//     sums keep f32 accuracy (gfx950's FP8 MFMA adds its 128 products in a
-//     narrower adder, about 2^-16 of the absolute sum, too coarse for an f32
-//     gradient).  A per-pair partial accumulator is rescaled by sL x sD and
-//     added to the total at each pair boundary.  Experts without rows get
-//     zeros.  The f32 output is written with 16-byte streaming stores.
+//     LDS), writes the scales and stores the 8-bit codes row-major into the
+//     pair's slab of the workspace ([512 rows][columns], rows past the pair's
+//     end up to the next multiple of 64 hold zero codes).
+//  2. gemm: persistent, one block per CU, walking its share of the work
+//     items (expert, 256-row k tile, 128-column n tile); an item covers the
+//     expert's pairs 64 rows at a time.  The code chunks of both operands are
+//     copied HBM -> LDS by buffer loads with an LDS destination through a
+//     five-stage ring that runs across pairs and items, so copy latency is
+//     paid once per block rather than once per tile.  The contraction runs
+//     over rows, which is the slow axis of both tiles, so the MFMA operands
+//     are read with the transposing ds_read_tr8_b64 (8 consecutive rows of
+//     one column per lane) and widened to bf16 exactly.  bf16 MFMA (every
+//     e4m3/e5m2 value is exact in bf16 and products are exact in f32) keeps
+//     f32 accuracy; gfx950's FP8 MFMA adds its 128 products in a narrower
+//     adder, about 2^-16 of the absolute sum, too coarse for an f32 gradient.
+//     Eight waves (two per SIMD) own 64 x 64 of the tile each; a per-pair
+//     partial accumulator is rescaled by sL x sD and added to the total at
+//     the pair's end.  Experts without rows get zeros.  The f32 output is
+//     written with 16-byte streaming stores, which drain while the next item
+//     computes.
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <algorithm>
 
 namespace fp8gmm {
 namespace {
@@ -34,7 +45,6 @@ constexpr int kTileM = 512;       // rows per gm-tile (the only supported value)
 constexpr int kPrepCols = 64;     // columns per prep block
 constexpr int kChunk = 64;        // contraction rows per GEMM stage
 constexpr int kThreads = 256;
-constexpr int kLdsStride = kTileM + 8;   // bf16 elements per transposed LDS row (prep)
 
 // Pair table from group_sizes, built by wave 0 into LDS: for pair p (in
 // (expert, tile) order) its expert, first row and row count; returns via
@@ -100,12 +110,11 @@ template <bool GRAD_E5M2>
 __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __restrict__ lhs,
                                                              const uint16_t* __restrict__ dout,
                                                              const int* __restrict__ group_sizes, int G, int M,
-                                                             int K, int N, uint16_t* __restrict__ lt,
-                                                             uint16_t* __restrict__ dt, float* __restrict__ sl,
+                                                             int K, int N, uint8_t* __restrict__ ql,
+                                                             uint8_t* __restrict__ qd, float* __restrict__ sl,
                                                              float* __restrict__ sd, int* status) {
   __shared__ int g_start[kMaxGroups], g_end[kMaxGroups], p_base[kMaxGroups + 1];
   __shared__ float red[4][kPrepCols];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kPrepCols * kLdsStride];
   PairTable pt{g_start, g_end, p_base};
   build_pair_table(group_sizes, G, M, pt, blockIdx.y == 0 ? status : nullptr);
   __syncthreads();
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
   for (int i = 0; i < 16; ++i) {
     const int r = rr + 32 * i;
     if (r < R) {
-      x[i] = *reinterpret_cast<const v4i*>(src + (size_t)(r0 + r) * cols + c0 + cg * 8);
+      x[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + (size_t)(r0 + r) * cols + c0 + cg * 8));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         am[2 * e] = __builtin_fmaxf(am[2 * e], __builtin_fabsf(bf16_lo((uint32_t)x[i][e])));
@@ -173,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
     float* sdst = is_l ? sl + (size_t)p * K : sd + (size_t)p * N;
     sdst[c0 + tid] = __builtin_fmaxf(a, kAmaxFloor) / fmax;
   }
-  // ---- quantize, decode exactly, store transposed as bf16
+  // ---- quantize (f32 quotient, saturating RNE) and store the codes row-major in the pair's slab
+  uint8_t* dst = (is_l ? ql + (size_t)p * kTileM * K : qd + (size_t)p * kTileM * N) + c0 + cg * 8;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = rr + 32 * i;
@@ -184,50 +194,93 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
         q[2 * e] = bf16_lo((uint32_t)x[i][e]) / s[2 * e];
         q[2 * e + 1] = bf16_hi((uint32_t)x[i][e]) / s[2 * e + 1];
       }
-      uint32_t w0, w1;
-      v2f d[4];
+      v2i w;
       if (is_l || !GRAD_E5M2) {
-        w0 = cvt_e4m3x4(q[0], q[1], q[2], q[3]);
-        w1 = cvt_e4m3x4(q[4], q[5], q[6], q[7]);
-        d[0] = dec_e4m3x2<false>(w0); d[1] = dec_e4m3x2<true>(w0);
-        d[2] = dec_e4m3x2<false>(w1); d[3] = dec_e4m3x2<true>(w1);
+        w[0] = (int)cvt_e4m3x4(q[0], q[1], q[2], q[3]);
+        w[1] = (int)cvt_e4m3x4(q[4], q[5], q[6], q[7]);
       } else {
-        w0 = cvt_e5m2x4(q[0], q[1], q[2], q[3]);
-        w1 = cvt_e5m2x4(q[4], q[5], q[6], q[7]);
-        d[0] = dec_e5m2x2<false>(w0); d[1] = dec_e5m2x2<true>(w0);
-        d[2] = dec_e5m2x2<false>(w1); d[3] = dec_e5m2x2<true>(w1);
+        w[0] = (int)cvt_e5m2x4(q[0], q[1], q[2], q[3]);
+        w[1] = (int)cvt_e5m2x4(q[4], q[5], q[6], q[7]);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // decoded 8-bit values have at most 4 significant bits: the bf16 is the f32's high half
-        const float v = (r < R) ? d[e >> 1][e & 1] : 0.0f;
-        tile[(cg * 8 + e) * kLdsStride + r] = (uint16_t)(__float_as_uint(v) >> 16);
-      }
+      if (r >= R) w = (v2i){0, 0};
+      *reinterpret_cast<v2i*>(dst + (size_t)r * cols) = w;
     }
-  }
-  __syncthreads();
-  // ---- write [64 columns][Rpad rows] to the transposed workspace
-  uint16_t* dst = (is_l ? lt + ((size_t)p * K + c0) * kTileM : dt + ((size_t)p * N + c0) * kTileM);
-  const int vec_per_col = Rpad / 8;
-  for (int v = tid; v < kPrepCols * vec_per_col; v += kThreads) {
-    const int c = v / vec_per_col, r = (v % vec_per_col) * 8;
-    const v4i val = *reinterpret_cast<const v4i*>(&tile[c * kLdsStride + r]);
-    *reinterpret_cast<v4i*>(dst + (size_t)c * kTileM + r) = val;
   }
 }
 
 // ------------------------------------------------------------------ gemm
 
-constexpr int BMK = 256;   // k rows of drhs per block
-constexpr int BNN = 128;   // n columns per block
-constexpr int kRowB = kChunk * 2;                     // 128 bytes per LDS row
-constexpr int kStageG = (BMK + BNN) * kRowB;          // 48 KiB
-constexpr int kLdsG = 2 * kStageG;
+constexpr int BMK = 256;                        // drhs rows (k) per block
+constexpr int BNN = 128;                        // drhs columns (n) per block
+constexpr int kGThreads = 512;                  // 8 waves: 4 along k x 2 along n, 64 x 64 each
+constexpr int kAStage = kChunk * BMK;           // qL codes [64 rows][256 k]
+constexpr int kBStage = kChunk * BNN;           // qD codes [64 rows][128 n]
+constexpr int kStageG = kAStage + kBStage;      // 24 KiB
+constexpr int kStagesG = 5;
+constexpr int kLdsG = kStagesG * kStageG;
+constexpr int kALoadsG = kAStage / (8 * 1024);  // 1 KB wave-wide loads per wave per stage
+constexpr int kBLoadsG = kBStage / (8 * 1024);
+constexpr int kLoadsG = kALoadsG + kBLoadsG;
 
-__device__ __forceinline__ int g_swz(int row, int chunk) { return row * kRowB + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk swizzles: the 16 lanes of a transposing read touch 8
+// consecutive rows at one chunk, and two such groups are served together.
+__device__ __forceinline__ int l_slot(int row, int chunk) { return row * BMK + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int d_slot(int row, int chunk) { return row * BNN + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void tgmm_gemm_kernel(const uint16_t* __restrict__ lt, const uint16_t* __restrict__ dt,
+// 8 codes (8 consecutive rows of one column) -> 8 bf16, exactly.
+template <bool E5M2>
+__device__ __forceinline__ v4i widen8(const v2i& c) {
+  v4i o;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    v2bf lo, hi;
+    if (E5M2) {
+      lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(c[d], 1.0f, false);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(c[d], 1.0f, true);
+    } else {
+      lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[d], 1.0f, false);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[d], 1.0f, true);
+    }
+    o[2 * d] = __builtin_bit_cast(int, lo);
+    o[2 * d + 1] = __builtin_bit_cast(int, hi);
+  }
+  return o;
+}
+
+// One 64-row stage: optionally start the copy of a later stage into `wr`,
+// then read this stage's operands from `rd` and run its 32 MFMAs per wave.
+// `wr` and `rd` are distinct ring slots; marking them __restrict__ lets the
+// compiler see that the reads cannot depend on the copy just issued, so it
+// adds no wait for it (the kernel's own wait + barrier order the ring).
+template <bool GRAD_E5M2>
+__device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, bool copy,
+                                           BufRsrc ra, BufRsrc rb, const uint32_t* va, const uint32_t* vb,
+                                           uint32_t soa, uint32_t sob, int wave, const int* a_rd, const int* b_rd,
+                                           v4f (&part)[4][4]) {
+  if (copy) {
+#pragma unroll
+    for (int j = 0; j < kALoadsG; ++j) dma16(ra, wr + (kALoadsG * wave + j) * 1024, va[j], soa);
+#pragma unroll
+    for (int j = 0; j < kBLoadsG; ++j) dma16(rb, wr + kAStage + (kBLoadsG * wave + j) * 1024, vb[j], sob);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v4i bo[4], ao[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bo[j] = widen8<GRAD_E5M2>(lds_read_tr8(rd + b_rd[j] + s * 32 * BNN));
+#pragma unroll
+    for (int f = 0; f < 4; ++f) ao[f] = widen8<false>(lds_read_tr8(rd + a_rd[f] + s * 32 * BMK));
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        part[f][j] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, bo[j]), __builtin_bit_cast(v8bf, ao[f]), part[f][j]);
+  }
+}
+
+template <bool GRAD_E5M2>
+__global__ __attribute__((amdgpu_flat_work_group_size(kGThreads, kGThreads), amdgpu_waves_per_eu(2, 2)))
+void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict__ qd,
                       const float* __restrict__ sl, const float* __restrict__ sd,
                       const int* __restrict__ group_sizes, int G, int M, int K, int N,
                       float* __restrict__ drhs) {
@@ -235,138 +288,175 @@ void tgmm_gemm_kernel(const uint16_t* __restrict__ lt, const uint16_t* __restric
   int* g_start = reinterpret_cast<int*>(smem + kLdsG);
   int* g_end = g_start + G;
   int* p_base = g_end + G;
+  int* g_chunks = p_base + G + 1;     // 64-row chunks of each expert (all its pairs)
   PairTable pt{g_start, g_end, p_base};
   build_pair_table(group_sizes, G, M, pt, nullptr);
   __syncthreads();
+  auto nchunks = [&](int g, int p) {
+    int r0, r1;
+    pair_rows(pt, g, p, r0, r1);
+    return (r1 - r0 + kChunk - 1) / kChunk;
+  };
+  for (int g = threadIdx.x; g < G; g += kGThreads) {
+    int c = 0;
+    for (int p = p_base[g]; p < p_base[g + 1]; ++p) c += nchunks(g, p);
+    g_chunks[g] = c;
+  }
+  __syncthreads();
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave >> 1, wn = wave & 1;
   const int kt_n = K / BMK, nt_n = N / BNN;
-  // blocks of one expert are adjacent; within it k tiles vary fastest so the
-  // 8 XCDs share the dout tile of the same n tile
-  const int bid = blockIdx.x;
-  const int g = bid / (kt_n * nt_n);
-  const int rem = bid % (kt_n * nt_n);
-  const int kt = rem % kt_n, nt = rem / kt_n;
-  float* out = drhs + ((size_t)g * K + (size_t)kt * BMK) * N + (size_t)nt * BNN;
+  const int per_g = kt_n * nt_n;
+  // work item = (expert, n tile, k tile fastest); block b takes items b,
+  // b + gridDim.x, ...  Items of one expert are spread over every block (and
+  // so over every XCD), which keeps the work balanced however skewed the
+  // expert sizes are.
+  const int total = G * per_g;
+  const int stride = gridDim.x;
 
-  v4f tot[8][4];
+  // ---- per-lane copy offsets within a chunk (item-independent part) and operand read offsets
+  uint32_t va[kALoadsG], vb[kBLoadsG];
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int j = 0; j < kALoadsG; ++j) {
+    const int row = (kALoadsG * wave + j) * 4 + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);
+    va[j] = (uint32_t)row * (uint32_t)K + (uint32_t)(ch * 16);
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tot[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kBLoadsG; ++j) {
+    const int row = (kBLoadsG * wave + j) * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);
+    vb[j] = (uint32_t)row * (uint32_t)N + (uint32_t)(ch * 16);
+  }
+  const int Lg = lane & 15;
+  const int rbase = (lane >> 4) * 8 + (Lg >> 1);      // + 32 * s
+  int a_rd[4], b_rd[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) a_rd[f] = l_slot(rbase, wk * 4 + f) + 8 * (Lg & 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b_rd[j] = kAStage + d_slot(rbase, wn * 4 + j) + 8 * (Lg & 1);
 
-  const int p0 = p_base[g], p1 = p_base[g + 1];
-  if (p1 > p0) {
-    // per-thread load slots: A (lt) 8 x 16 B, B (dt) 4 x 16 B per stage
-    int a_off[8], b_off[4];
-    size_t a_src[8], b_src[4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = tid + kThreads * j;
-      const int row = i >> 3, c = i & 7;
-      a_src[j] = (size_t)(kt * BMK + row) * kTileM + c * 8;
-      a_off[j] = g_swz(row, c);
+  // ---- copy side: the next (item, pair, chunk) to copy, stages run ahead of the compute side
+  int ii = blockIdx.x, ig = 0, ikt = 0, int_ = 0, ip = 0, ip1 = 0, ic = 0, inc = 0;
+  auto seek = [&]() {   // first item at or after ii that has rows
+    while (ii < total && g_chunks[ii / per_g] == 0) ii += stride;
+    if (ii < total) {
+      ig = __builtin_amdgcn_readfirstlane(ii / per_g);
+      const int rem = ii % per_g;
+      ikt = rem % kt_n;
+      int_ = rem / kt_n;
+      ip = __builtin_amdgcn_readfirstlane(p_base[ig]);
+      ip1 = __builtin_amdgcn_readfirstlane(p_base[ig + 1]);
+      ic = 0;
+      inc = __builtin_amdgcn_readfirstlane(nchunks(ig, ip));
     }
+  };
+  int tI = 0;
+  // copy parameters of the next chunk (ii, ip, ic)
+  auto copy_rsrc_a = [&]() { return make_rsrc(ql + (size_t)ip * kTileM * K, (uint32_t)kTileM * (uint32_t)K); };
+  auto copy_rsrc_b = [&]() { return make_rsrc(qd + (size_t)ip * kTileM * N, (uint32_t)kTileM * (uint32_t)N); };
+  uint32_t va_i[kALoadsG], vb_i[kBLoadsG];      // copy offsets with the item's column origin
+  auto set_item_offsets = [&]() {
+#pragma unroll
+    for (int j = 0; j < kALoadsG; ++j) va_i[j] = va[j] + (uint32_t)ikt * BMK;
+#pragma unroll
+    for (int j = 0; j < kBLoadsG; ++j) vb_i[j] = vb[j] + (uint32_t)int_ * BNN;
+  };
+  auto advance = [&]() {
+    ++tI;
+    if (++ic == inc) {
+      ic = 0;
+      if (++ip == ip1) {
+        ii += stride;
+        seek();
+        set_item_offsets();
+      } else {
+        inc = __builtin_amdgcn_readfirstlane(nchunks(ig, ip));
+      }
+    }
+  };
+  auto issue = [&]() {          // prologue copies (nothing is read yet)
+    uint8_t* St = smem + (tI % kStagesG) * kStageG;
+    const BufRsrc ra = copy_rsrc_a(), rb = copy_rsrc_b();
+#pragma unroll
+    for (int j = 0; j < kALoadsG; ++j)
+      dma16(ra, St + (kALoadsG * wave + j) * 1024, va_i[j], (uint32_t)ic * kChunk * (uint32_t)K);
+#pragma unroll
+    for (int j = 0; j < kBLoadsG; ++j)
+      dma16(rb, St + kAStage + (kBLoadsG * wave + j) * 1024, vb_i[j], (uint32_t)ic * kChunk * (uint32_t)N);
+    advance();
+  };
+  seek();
+  set_item_offsets();
+  for (int t = 0; t < kStagesG - 1 && ii < total; ++t) issue();
+
+  // ---- compute side
+  v4f tot[4][4], part[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = tid + kThreads * j;
-      const int row = i >> 3, c = i & 7;
-      b_src[j] = (size_t)(nt * BNN + row) * kTileM + c * 8;
-      b_off[j] = BMK * kRowB + g_swz(row, c);
+      tot[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
-    int a_rd[8][2], b_rd[4][2];
+  int tC = 0;
+  for (int ci = blockIdx.x; ci < total; ci += stride) {
+    const int g = __builtin_amdgcn_readfirstlane(ci / per_g);
+    const int rem = ci % per_g;
+    const int kt = rem % kt_n, nt = rem / kt_n;
+    const int p_end = __builtin_amdgcn_readfirstlane(p_base[g + 1]);
+    for (int p = __builtin_amdgcn_readfirstlane(p_base[g]); p < p_end; ++p) {
+      // this pair's scales, needed when its last chunk is done
+      float slv[4];
+      v4f sdv[4];
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
+      for (int f = 0; f < 4; ++f) slv[f] = sl[(size_t)p * K + kt * BMK + wk * 64 + f * 16 + Lg];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) a_rd[f][s] = g_swz(wk * 128 + f * 16 + (lane & 15), s * 4 + (lane >> 4));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        b_rd[j][s] = BMK * kRowB + g_swz(wn * 64 + j * 16 + (lane & 15), s * 4 + (lane >> 4));
-
-    v4i sa[8], sb[4];
-    // flattened (pair, chunk) sequence of this expert
-    auto chunks_of = [&](int p) {
-      int r0, r1;
-      pair_rows(pt, g, p, r0, r1);
-      return (r1 - r0 + kChunk - 1) / kChunk;
-    };
-    auto load = [&](int p, int c) {
-      const uint16_t* lp = lt + (size_t)p * K * kTileM + c * kChunk;
-      const uint16_t* dp = dt + (size_t)p * N * kTileM + c * kChunk;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sa[j] = *reinterpret_cast<const v4i*>(lp + a_src[j]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sb[j] = *reinterpret_cast<const v4i*>(dp + b_src[j]);
-    };
-    auto store = [&](int buf) {
-      uint8_t* S = smem + buf * kStageG;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<v4i*>(S + a_off[j]) = sa[j];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(S + b_off[j]) = sb[j];
-    };
-
-    int p = p0, c = 0, nc = chunks_of(p0);
-    load(p, c);
-    store(0);
-    __syncthreads();
-    int buf = 0;
-    v4f part[8][4];
-#pragma unroll
-    for (int f = 0; f < 8; ++f)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-    while (true) {
-      // next (pair, chunk)
-      int pn = p, cn = c + 1, ncn = nc;
-      if (cn == nc) { pn = p + 1; cn = 0; ncn = pn < p1 ? chunks_of(pn) : 0; }
-      const bool more = pn < p1;
-      if (more) load(pn, cn);
-      const uint8_t* S = smem + buf * kStageG;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        v8bf bfr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const v8bf*>(S + b_rd[j][s]);
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-          const v8bf af = *reinterpret_cast<const v8bf*>(S + a_rd[f][s]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) part[f][j] = mfma_bf16_16x16x32(bfr[j], af, part[f][j]);
-        }
+      for (int j = 0; j < 4; ++j)
+        sdv[j] = *reinterpret_cast<const v4f*>(sd + (size_t)p * N + nt * BNN + wn * 64 + j * 16 + 4 * (lane >> 4));
+      const int nc = __builtin_amdgcn_readfirstlane(nchunks(g, p));
+      for (int c = 0; c < nc; ++c, ++tC) {
+        // stage tC landed in every wave's copy (only the copies issued after
+        // it may still be in flight; other loads and stores only make the
+        // wait stricter); stage tC-1's buffer is free for the next copy
+        const int pending = tI - 1 - tC;
+        static_assert(kStagesG <= 6, "one wait per possible count below");
+        if (pending >= 4) wait_vmem_lds<4 * kLoadsG>();
+        else if (pending == 3) wait_vmem_lds<3 * kLoadsG>();
+        else if (pending == 2) wait_vmem_lds<2 * kLoadsG>();
+        else if (pending == 1) wait_vmem_lds<kLoadsG>();
+        else wait_vmem_lds<0>();
+        barrier_only();
+        const bool copy = ii < total;
+        tgmm_stage<GRAD_E5M2>(smem + (tI % kStagesG) * kStageG, smem + (tC % kStagesG) * kStageG, copy,
+                              copy_rsrc_a(), copy_rsrc_b(), va_i, vb_i, (uint32_t)ic * kChunk * (uint32_t)K,
+                              (uint32_t)ic * kChunk * (uint32_t)N, wave, a_rd, b_rd, part);
+        if (copy) advance();
       }
-      if (cn == 0) {
-        // pair p complete: total += partial * sL[k] * sD[n]
-        const float* slp = sl + (size_t)p * K + kt * BMK + wk * 128 + (lane & 15);
-        const float* sdp = sd + (size_t)p * N + nt * BNN + wn * 64 + 4 * (lane >> 4);
+      // pair complete: total += partial * sL[k] * sD[n]
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const v4f dsc = *reinterpret_cast<const v4f*>(sdp + j * 16);
 #pragma unroll
-          for (int f = 0; f < 8; ++f) {
-            const float lsc = slp[f * 16];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) tot[f][j][r] += (part[f][j][r] * lsc) * dsc[r];
-            part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-          }
+          for (int r = 0; r < 4; ++r) tot[f][j][r] = __builtin_fmaf(part[f][j][r] * slv[f], sdv[j][r], tot[f][j][r]);
+          part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
         }
-      }
-      if (!more) break;
-      store(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-      p = pn; c = cn; nc = ncn;
     }
-  }
-  // ---- store: lane owns k = wk*128 + f*16 + lane%16, n = wn*64 + j*16 + 4*(lane/16) + 0..3
+    // ---- store the tile (zeros for an expert without rows):
+    // lane owns k = wk*64 + f*16 + lane%16, n = wn*64 + j*16 + 4*(lane/16) + 0..3
+    float* out = drhs + ((size_t)g * K + (size_t)kt * BMK) * N + (size_t)nt * BNN;
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    float* orow = out + (size_t)(wk * 128 + f * 16 + (lane & 15)) * N + wn * 64 + 4 * (lane >> 4);
+    for (int f = 0; f < 4; ++f) {
+      float* orow = out + (size_t)(wk * 64 + f * 16 + (lane & 15)) * N + wn * 64 + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(tot[f][j], reinterpret_cast<v4f*>(orow + j * 16));
+      for (int j = 0; j < 4; ++j) {
+        __builtin_nontemporal_store(tot[f][j], reinterpret_cast<v4f*>(orow + j * 16));
+        tot[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      }
+    }
   }
 }
 
@@ -377,7 +467,7 @@ size_t tgmm_workspace_bytes(long long M, long long K, long long N, int G) {
   if (tmax <= 0) return 0;
   const size_t a = 256;
   auto al = [&](size_t x) { return (x + a - 1) / a * a; };
-  return al((size_t)tmax * K * kTileM * 2) + al((size_t)tmax * N * kTileM * 2) + al((size_t)tmax * K * 4) +
+  return al((size_t)tmax * kTileM * K) + al((size_t)tmax * kTileM * N) + al((size_t)tmax * K * 4) +
          al((size_t)tmax * N * 4);
 }
 
@@ -388,9 +478,9 @@ hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const in
   const size_t a = 256;
   auto al = [&](size_t x) { return (x + a - 1) / a * a; };
   uint8_t* base = static_cast<uint8_t*>(ws);
-  uint16_t* lt = reinterpret_cast<uint16_t*>(base);
-  uint16_t* dt = reinterpret_cast<uint16_t*>(base + al((size_t)tmax * K * kTileM * 2));
-  float* sl = reinterpret_cast<float*>(base + al((size_t)tmax * K * kTileM * 2) + al((size_t)tmax * N * kTileM * 2));
+  uint8_t* ql = base;
+  uint8_t* qd = base + al((size_t)tmax * kTileM * K);
+  float* sl = reinterpret_cast<float*>(qd + al((size_t)tmax * kTileM * N));
   float* sd = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sl) + al((size_t)tmax * K * 4));
   if (dbg_sl) sl = dbg_sl;
   if (dbg_sd) sd = dbg_sd;
@@ -398,16 +488,22 @@ hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const in
     dim3 grid((unsigned)tmax, (unsigned)(K / kPrepCols + N / kPrepCols));
     if (grad_e5m2)
       hipLaunchKernelGGL(tgmm_prep_kernel<true>, grid, dim3(kThreads), 0, stream, lhs, dout, group_sizes, G, M, K,
-                         N, lt, dt, sl, sd, status);
+                         N, ql, qd, sl, sd, status);
     else
       hipLaunchKernelGGL(tgmm_prep_kernel<false>, grid, dim3(kThreads), 0, stream, lhs, dout, group_sizes, G, M, K,
-                         N, lt, dt, sl, sd, status);
+                         N, ql, qd, sl, sd, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t lds = kLdsG + sizeof(int) * (3 * (size_t)G + 1);
-  hipLaunchKernelGGL(tgmm_gemm_kernel, dim3((unsigned)((long long)G * (K / BMK) * (N / BNN))), dim3(kThreads), lds,
-                     stream, lt, dt, sl, sd, group_sizes, G, M, K, N, drhs);
+  const size_t lds = kLdsG + sizeof(int) * (4 * (size_t)G + 1);
+  const long long items = (long long)G * (K / BMK) * (N / BNN);
+  const dim3 grid((unsigned)std::min<long long>(items, device_cu_count()));   // one resident block per CU
+  if (grad_e5m2)
+    hipLaunchKernelGGL(tgmm_gemm_kernel<true>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G, M,
+                       K, N, drhs);
+  else
+    hipLaunchKernelGGL(tgmm_gemm_kernel<false>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G,
+                       M, K, N, drhs);
   return hipGetLastError();
 }
 

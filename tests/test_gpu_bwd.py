@@ -198,3 +198,31 @@ def test_tgmm_config4_sampled(grad):
         assert not torch.any(drhs[int(g)] != 0)
     assert torch.isfinite(drhs).all()
     print(f"tgmm config4 {grad}: rel fro {tot:.2e} (max per expert {per:.2e})")
+
+
+@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
+def test_tgmm_every_code(grad):
+    """Every finite code of both operands passes through the GEMM: row 0 holds
+    the format's largest value in every column, so each tile-channel scale is
+    exactly 1 and each other entry (an exactly representable 8-bit value)
+    quantizes to its own code; the result is compared with the oracle."""
+    M, K, N = 512, 256, 128
+    gfmt = F.E5M2 if grad == "e5m2" else F.E4M3
+
+    def column_block(fmt, cols, shift):
+        codes = np.array([c for c in range(256) if np.isfinite(F.DECODE[fmt][c])], np.uint8)
+        idx = (np.arange(M - 1)[:, None] * 7 + np.arange(cols)[None, :] * shift) % len(codes)
+        vals = F.DECODE[fmt][codes[idx]]
+        top = np.full((1, cols), F.DECODE[fmt][F.MAX_CODE[fmt]])
+        return F.f64_to_bf16_bits(np.vstack([top, vals])), len(codes)
+
+    lhs, nl = column_block(F.E4M3, K, 3)
+    dout, nd = column_block(gfmt, N, 5)
+    assert nl == 254 and nd == (248 if grad == "e5m2" else 254)
+    (drhs, sL, sD), st = run_tgmm(lhs, dout, [M], grad)
+    assert st == 0
+    ref = O.tgmm_quant(lhs, dout, [M], grad, 512)
+    assert np.all(ref.sL == 1.0) and np.all(ref.sD == 1.0)
+    assert np.array_equal(sL.cpu().numpy()[:1], ref.sL) and np.array_equal(sD.cpu().numpy()[:1], ref.sD)
+    tot, per = check_f32(drhs.cpu().numpy(), ref.drhs_f64, ref.absum, None, np.array([M]), f"tgmm codes {grad}")
+    print(f"tgmm every code {grad}: rel fro {tot:.2e}")
