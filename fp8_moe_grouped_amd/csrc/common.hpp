@@ -86,6 +86,13 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b, c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// D = A(32x64 e4m3) * B(64x32 e4m3) + C, f32 accumulate.  Lane l holds row
+// l%32 of A (column l%32 of B) and the 32 k-values (l/32)*32 + 0..31; D: lane
+// l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+__device__ __forceinline__ v16f mfma_e4m3_32x32x64(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // D = A(16x32 bf16) * B(32x16 bf16) + C; lane l holds row l%16 of A (column
 // l%16 of B) and k-values (l/16)*8 + 0..7.
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f& c) {

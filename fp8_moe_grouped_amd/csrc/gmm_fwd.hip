@@ -9,24 +9,24 @@
 //
 // Tiling (gfx950): a block owns a 256-row x BN-column output tile of one
 // expert, BN = 256 (or 128 when N is not a multiple of 256; for SwiGLU 128
-// gate + the matching 128 up columns); four waves own 128 x BN/2 each, i.e.
-// 256 (or 128) f32 accumulators per lane held in AGPRs.  K advances 128 bytes
-// per step through two LDS stages:
+// gate + the matching 128 up columns).  Eight waves, two per SIMD, own
+// 64 x BN/2 each (128 or 64 f32 accumulators per lane); the second wave on
+// a SIMD issues MFMAs while the first waits on LDS or on its copies.  K
+// advances 64 bytes per stage through a four-stage LDS ring:
 //  * both tiles are copied HBM/L2 -> LDS by buffer loads with the LDS
-//    destination (no VGPR staging), issued at the top of the step for the next
-//    stage; per-lane offsets are fixed, one scalar offset advances per step;
+//    destination, issued four stages ahead and spread over the MFMAs of a
+//    stage (a stage's buffer is free once its operands are in registers);
 //  * the activation tile is row-major, the weight tile keeps the natural
 //    [k][n] layout; 16-byte chunks are XOR-swizzled so that the operand reads
-//    hit distinct banks (gfx950 LDS serves 256 bytes per cycle);
-//  * the weight operand is read with the transposing ds_read_tr8_b64, which
-//    hands each lane 8 consecutive k of one column, so the N-contiguous codes
-//    need no transpose pass;
-//  * activation fragment f+1 is read while the 8 MFMAs of fragment f run, and
-//    after a mid-step barrier the next stage's weight fragments are read while
-//    the last two fragment groups run; scheduling fences keep this order.
-// The MFMA is issued with the weight as its first operand, which makes each
-// lane own four consecutive output columns of one row: the epilogue scales,
-// optionally applies SwiGLU, and stores 8-byte bf16 groups.
+//    hit distinct banks;
+//  * the weight operand is read with the transposing ds_read_tr8_b64 (8
+//    consecutive k of one column per lane), so the N-contiguous codes need no
+//    transpose pass;
+//  * one barrier per stage; after it each operand fragment of the next stage
+//    is reread in place right after the last MFMA that uses the current one.
+// The 32x32x64 MFMA takes the weight as its first operand, which makes each
+// lane own one row and groups of four consecutive output columns: the
+// epilogue scales, optionally applies SwiGLU, and stores 8-byte bf16 groups.
 //
 // Scheduling: every block rebuilds the expert table from group_sizes (a wave
 // scan), maps its id to a (global m-tile, n-tile) pair with an XCD-aware,
@@ -36,42 +36,47 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace fp8gmm {
 namespace {
 
 constexpr int BM = 256;
-constexpr int BK = 128;
-constexpr int kThreads = 256;
+constexpr int BK = 64;              // K bytes per stage
+constexpr int kStages = 4;
+constexpr int kThreads = 512;       // 8 waves, two per SIMD
 constexpr int kGroupM = 8;
 
 template <int BN>
 constexpr int stage_bytes() { return BM * BK + BK * BN; }
 template <int BN>
-constexpr int lds_main() { return 2 * stage_bytes<BN>(); }   // double buffered
+constexpr int lds_main() { return kStages * stage_bytes<BN>(); }
 
-// 16-byte chunk swizzles (bank-conflict free operand reads on 64 banks).
-__device__ __forceinline__ int a_key(int row) { return (row >> 1) & 7; }
+// 16-byte chunk swizzles: 16 lanes reading 16 consecutive activation rows at
+// one chunk, and two transposing-read groups (8 weight rows each, adjacent
+// chunks), hit distinct banks.
+__device__ __forceinline__ int a_swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 template <int BN>
-__device__ __forceinline__ int b_key(int kk) {
-  return BN == 256 ? ((kk & 7) | (((kk >> 5) & 1) << 3)) : (((kk >> 1) & 3) | (((kk >> 5) & 1) << 2));
-}
-__device__ __forceinline__ int a_swz(int row, int chunk) { return row * BK + ((chunk ^ a_key(row)) << 4); }
+__device__ __forceinline__ int b_key(int k) { return BN == 256 ? ((k & 7) << 1) : (((k >> 1) & 3) << 1); }
 template <int BN>
-__device__ __forceinline__ int b_swz(int kk, int chunk) { return kk * BN + ((chunk ^ b_key<BN>(kk)) << 4); }
+__device__ __forceinline__ int b_swz(int k, int chunk) { return k * BN + ((chunk ^ b_key<BN>(k)) << 4); }
 
-// NJ: 16-column MFMA fragments per wave along N (8 -> BN = 256, 4 -> BN = 128).
-template <bool SWIGLU, int NJ>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+template <bool SWIGLU, int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict__ ascale,
                         const uint8_t* __restrict__ codes, const float* __restrict__ wscale,
                         const int* __restrict__ group_sizes, int G, int M, int K, int N,
                         uint16_t* __restrict__ out, int* status) {
-  constexpr int BN = 32 * NJ;
+  constexpr int NJ = BN / 64;                       // 32-column fragments per wave (BN/2 columns)
+  constexpr int MI = 2;                             // 32-row fragments per wave (64 rows)
   constexpr int kStageBytes = stage_bytes<BN>();
-  constexpr int kBChunksRow = BN / 16;                  // 16-byte chunks per weight-tile row
-  constexpr int kBLoads = BK * kBChunksRow / kThreads;  // weight chunks per thread per stage
-  constexpr int kBRowsPerLoad = 1024 / BN;              // weight rows per wave-wide load
-  static_assert(!SWIGLU || NJ == 8, "SwiGLU pairs 4 gate with 4 up fragments");
+  constexpr int kBChunks = BN / 16;                 // 16-byte chunks per weight-tile row
+  constexpr int kALoads = BM * BK / 1024 / 8;       // 1 KB wave-wide copies per wave per stage
+  constexpr int kBLoads = BK * BN / 1024 / 8;
+  constexpr int kLoads = kALoads + kBLoads;
+  constexpr int kBRowsPerLoad = 1024 / BN;
+  static_assert(!SWIGLU || BN == 256, "SwiGLU pairs 2 gate with 2 up fragments per wave");
+  static_assert(kLoads * (kStages - 1) < 64, "outstanding copies fit vmcnt");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* t_start = reinterpret_cast<int*>(smem + lds_main<BN>());
   int* t_end = t_start + G;
@@ -82,7 +87,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;          // 4 x 2 waves
   const int I = N >> 1;
   const int n_tiles = SWIGLU ? (I / (BN / 2)) : (N / BN);
   const int T = t_pre[G];
@@ -105,169 +110,181 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   // ---- buffer resources: the tile's activation rows and the expert's codes
   const BufRsrc ra = make_rsrc(aq + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
   const BufRsrc rb = make_rsrc(codes + (size_t)g * K * N, (uint32_t)K * (uint32_t)N);
-  uint32_t va[8];                      // activation chunk offsets (step 0)
+  uint32_t va[kALoads];                // activation chunk offsets (stage 0)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * (8 * wave + j) + (lane >> 3);
-    const int c = (lane & 7) ^ a_key(r);
+  for (int j = 0; j < kALoads; ++j) {
+    const int r = (kALoads * wave + j) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     va[j] = (uint32_t)min(r, rows - 1) * (uint32_t)K + (uint32_t)(c << 4);
   }
-  uint32_t vb[kBLoads];                // weight chunk offsets (step 0)
+  uint32_t vb[kBLoads];                // weight chunk offsets (stage 0)
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j) {
-    const int kk = kBRowsPerLoad * (kBLoads * wave + j) + lane / kBChunksRow;
-    const int c = (lane % kBChunksRow) ^ b_key<BN>(kk);
+    const int kk = (kBLoads * wave + j) * kBRowsPerLoad + lane / kBChunks;
+    const int c = (lane % kBChunks) ^ b_key<BN>(kk);
     int col;
     if (SWIGLU) col = (c < 8) ? nt * (BN / 2) + (c << 4) : I + nt * (BN / 2) + ((c - 8) << 4);
     else col = nt * BN + (c << 4);
     vb[j] = (uint32_t)kk * (uint32_t)N + (uint32_t)col;
   }
-  const uint32_t b_step = (uint32_t)BK * (uint32_t)N;
 
-  // ---- per-lane LDS read offsets of the MFMA operands
-  int a_rd[8][2];
+  // ---- per-lane LDS read offsets of the MFMA operands (within a stage)
+  int a_rd[2];                         // + i * 32 rows
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int r = wm * 128 + f * 16 + (lane & 15);
-    const int c0 = (lane >> 4) * 2;
-    a_rd[f][0] = a_swz(r, c0);
-    a_rd[f][1] = a_swz(r, c0 + 1);
-  }
-  int b_rd[NJ][4];
+  for (int h = 0; h < 2; ++h) a_rd[h] = a_swz(wm * 64 + (lane & 31), 2 * (lane >> 5) + h);
+  int b_rd[NJ];                        // + t * 8 rows
+  {
+    const int gq = lane >> 4, Lg = lane & 15;
+    const int kk = (gq >> 1) * 32 + (Lg >> 1);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    int cb;
-    if (SWIGLU) cb = (j < 4) ? wn * 64 + j * 16 : 128 + wn * 64 + (j - 4) * 16;
-    else cb = wn * (16 * NJ) + j * 16;
-    const int Lg = lane & 15;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int kk = (lane >> 4) * 32 + 8 * t + (Lg >> 1);
-      b_rd[j][t] = BM * BK + b_swz<BN>(kk, cb >> 4) + 8 * (Lg & 1);
+    for (int j = 0; j < NJ; ++j) {
+      int tc;                          // first tile column of fragment j
+      if (SWIGLU) tc = (j < 2) ? wn * 64 + 32 * j : 128 + wn * 64 + 32 * (j - 2);
+      else tc = wn * (BN / 2) + 32 * j;
+      b_rd[j] = BM * BK + b_swz<BN>(kk, (tc >> 4) + (gq & 1)) + 8 * (Lg & 1);
     }
   }
 
-  v4f acc[8][NJ];
-#pragma unroll
-  for (int f = 0; f < 8; ++f)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  const int nk = K / BK;
-  auto issue_stage = [&](int ks, int buf) {
-    uint8_t* S = smem + buf * kStageBytes;
-    const uint32_t sa = (uint32_t)ks * BK, sb = (uint32_t)ks * b_step;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(ra, S + (8 * wave + j) * 1024, va[j], sa);
-#pragma unroll
-    for (int j = 0; j < kBLoads; ++j) dma16(rb, S + BM * BK + (kBLoads * wave + j) * 1024, vb[j], sb);
+  auto issue_one = [&](uint8_t* S, int ks, int q) {   // copy number q (0 .. kLoads-1) of stage ks into S
+    if (q < kALoads) dma16(ra, S + (kALoads * wave + q) * 1024, va[q], (uint32_t)ks * BK);
+    else dma16(rb, S + BM * BK + (kBLoads * wave + q - kALoads) * 1024, vb[q - kALoads], (uint32_t)ks * BK * (uint32_t)N);
   };
-  auto read_a = [&](int buf, int f) {
-    const uint8_t* S = smem + buf * kStageBytes;
-    const v4i lo = *reinterpret_cast<const v4i*>(S + a_rd[f][0]);
-    const v4i hi = *reinterpret_cast<const v4i*>(S + a_rd[f][1]);
+  auto read_a = [&](const uint8_t* St, int i) {
+    const uint8_t* S = St + i * 32 * BK;
+    const v4i lo = *reinterpret_cast<const v4i*>(S + a_rd[0]);
+    const v4i hi = *reinterpret_cast<const v4i*>(S + a_rd[1]);
     return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  auto read_b = [&](int buf, v8i* bf) {
-    const uint8_t* S = smem + buf * kStageBytes;
+  auto read_b = [&](const uint8_t* St, int j) {
+    const uint8_t* S = St + b_rd[j];
+    v8i r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v2i v = lds_read_tr8(S + t * 8 * BN);
+      r[2 * t] = v[0];
+      r[2 * t + 1] = v[1];
+    }
+    return r;
+  };
+
+  v16f acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v2i v = lds_read_tr8(S + b_rd[j][t]);
-        bf[j][2 * t] = v[0];
-        bf[j][2 * t + 1] = v[1];
-      }
-  };
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // ---- prologue: stage 0 in LDS, its weight fragments and first activation fragment in registers
-  issue_stage(0, 0);
-  wait_vmem_all();
-  __syncthreads();
-  v8i bcur[NJ], bnxt[NJ];
-  read_b(0, bcur);
-  v8i acur = read_a(0, 0), anxt, a0n = acur;
+  const int nk = K / BK;
 
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) issue_stage(ks + 1, buf ^ 1);
+  // ---- prologue: stages 0..3 in flight, stage 0 landed and in registers
+  const int pre = min(nk, kStages);
+  for (int s = 0; s < pre; ++s)
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      if (f < 7) anxt = read_a(buf, f + 1);
-      if (f == 6 && more) {
-        // every wave's copy of stage ks+1 has landed: fetch its first fragments
-        wait_vmem_all();
-        __syncthreads();
-        read_b(buf ^ 1, bnxt);
-        a0n = read_a(buf ^ 1, 0);
-      }
+    for (int q = 0; q < kLoads; ++q) issue_one(smem + s * kStageBytes, s, q);
+  if (pre >= 4) wait_vmem_lds<3 * kLoads>();
+  else if (pre == 3) wait_vmem_lds<2 * kLoads>();
+  else if (pre == 2) wait_vmem_lds<kLoads>();
+  else wait_vmem_lds<0>();
+  barrier_only();
+  v8i a[MI], bf[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) a[i] = read_a(smem, i);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) bf[j] = read_b(smem, j);
+
+  // One stage.  ISSUE: copy stage ks+4 into this stage's buffer `wr` (its
+  // operands are in registers; the barrier makes sure every wave's are);
+  // MORE: stage ks+1 (buffer `rd`) exists and is reread into the registers as
+  // they free up; WAITN: copies issued after stage ks+1 that may still be in
+  // flight at the barrier.  `wr` and `rd` are distinct ring slots: marking them
+  // __restrict__ tells the compiler the reads cannot depend on the copies
+  // issued here, so it adds no wait for them (the wait + barrier above order
+  // the ring).
+  auto step = [&](int ks, auto issue_c, auto more_c, auto waitn_c, uint8_t* __restrict__ wr,
+                  const uint8_t* __restrict__ rd) {
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr bool MORE = decltype(more_c)::value;
+    constexpr int WAITN = decltype(waitn_c)::value;
+    v8i an[MI];
+    if (MORE) {
+      wait_vmem_lds<WAITN * kLoads>();
+      barrier_only();
+#pragma unroll
+      for (int i = 0; i < MI; ++i) an[i] = read_a(rd, i);
       sched_fence();
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[f][j] = mfma_e4m3_16x16x128(bcur[j], acur, acc[f][j]);
-      sched_fence();
-      if (f < 7) acur = anxt;
     }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) bcur[j] = bnxt[j];
-    acur = a0n;
-    __syncthreads();   // stage ks fully consumed before it is refilled
-  }
-
-  // ---- epilogue: lane owns row (f*16 + lane%16) and columns cb(j) + 4*(lane/16) + 0..3
-  const float* ws = wscale + (size_t)g * N;
-  if (SWIGLU) {
-    v4f sg[4], su[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cg = nt * (BN / 2) + wn * 64 + j * 16 + 4 * (lane >> 4);
-      sg[j] = *reinterpret_cast<const v4f*>(ws + cg);
-      su[j] = *reinterpret_cast<const v4f*>(ws + I + cg);
-    }
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int ml = wm * 128 + f * 16 + (lane & 15);
-      if (ml < rows) {
-        const int row = row0 + ml;
-        const float sr = ascale[row];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int cg = nt * (BN / 2) + wn * 64 + j * 16 + 4 * (lane >> 4);
-          float o[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float yg = (acc[f][j][r] * sr) * sg[j][r];
-            const float yu = (acc[f][j + 4][r] * sr) * su[j][r];
-            o[r] = yg / (1.0f + __expf(-yg)) * yu;
-          }
-          v2i pk;
-          pk[0] = (int)pack_bf16x2(o[0], o[1]);
-          pk[1] = (int)pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<v2i*>(out + (size_t)row * I + cg) = pk;
-        }
-      }
-    }
-  } else {
-    v4f sc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int c = nt * BN + wn * (16 * NJ) + j * 16 + 4 * (lane >> 4);
-      sc[j] = *reinterpret_cast<const v4f*>(ws + c);
+      if (ISSUE) {
+#pragma unroll
+        for (int q = j * kLoads / NJ; q < (j + 1) * kLoads / NJ; ++q) issue_one(wr, ks + kStages, q);
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[i][j] = mfma_e4m3_32x32x64(bf[j], a[i], acc[i][j]);
+      if (MORE) bf[j] = read_b(rd, j);
+      sched_fence();   // keep each refill between the MFMAs that surround it
     }
+    if (MORE) {
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int ml = wm * 128 + f * 16 + (lane & 15);
-      if (ml < rows) {
-        const int row = row0 + ml;
-        const float sr = ascale[row];
+      for (int i = 0; i < MI; ++i) a[i] = an[i];
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using W0 = std::integral_constant<int, 0>;
+  using W1 = std::integral_constant<int, 1>;
+  using W2 = std::integral_constant<int, 2>;
+  auto slot = [&](int s) { return smem + (s % kStages) * kStageBytes; };
+  int ks = 0;
+  for (; ks + kStages < nk; ++ks) step(ks, T_{}, T_{}, W2{}, slot(ks), slot(ks + 1));
+  if (ks + 3 < nk) { step(ks, F_{}, T_{}, W2{}, slot(ks), slot(ks + 1)); ++ks; }
+  if (ks + 2 < nk) { step(ks, F_{}, T_{}, W1{}, slot(ks), slot(ks + 1)); ++ks; }
+  if (ks + 1 < nk) { step(ks, F_{}, T_{}, W0{}, slot(ks), slot(ks + 1)); ++ks; }
+  step(ks, F_{}, F_{}, W0{}, slot(ks), slot(ks));
+
+  // ---- epilogue: lane owns row wm*64 + i*32 + lane%32 and, per fragment j,
+  // columns tc(j) + 8*q + 4*(lane/32) + 0..3 for q = 0..3
+  const float* ws = wscale + (size_t)g * N;
+  const int hl = 4 * (lane >> 5);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int c = nt * BN + wn * (16 * NJ) + j * 16 + 4 * (lane >> 4);
-          v2i pk;
-          pk[0] = (int)pack_bf16x2((acc[f][j][0] * sr) * sc[j][0], (acc[f][j][1] * sr) * sc[j][1]);
-          pk[1] = (int)pack_bf16x2((acc[f][j][2] * sr) * sc[j][2], (acc[f][j][3] * sr) * sc[j][3]);
-          *reinterpret_cast<v2i*>(out + (size_t)row * N + c) = pk;
-        }
+  for (int i = 0; i < MI; ++i) {
+    const int ml = wm * 64 + i * 32 + (lane & 31);
+    if (ml < rows) {
+      const int row = row0 + ml;
+      const float sr = ascale[row];
+      if (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = nt * (BN / 2) + wn * 64 + 32 * j + 8 * q + hl;
+            const v4f sg = *reinterpret_cast<const v4f*>(ws + c);
+            const v4f su = *reinterpret_cast<const v4f*>(ws + I + c);
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float yg = (acc[i][j][4 * q + e] * sr) * sg[e];
+              const float yu = (acc[i][j + 2][4 * q + e] * sr) * su[e];
+              o[e] = yg / (1.0f + __expf(-yg)) * yu;
+            }
+            v2i pk;
+            pk[0] = (int)pack_bf16x2(o[0], o[1]);
+            pk[1] = (int)pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<v2i*>(out + (size_t)row * I + c) = pk;
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = nt * BN + wn * (BN / 2) + 32 * j + 8 * q + hl;
+            const v4f sc = *reinterpret_cast<const v4f*>(ws + c);
+            v2i pk;
+            pk[0] = (int)pack_bf16x2((acc[i][j][4 * q] * sr) * sc[0], (acc[i][j][4 * q + 1] * sr) * sc[1]);
+            pk[1] = (int)pack_bf16x2((acc[i][j][4 * q + 2] * sr) * sc[2], (acc[i][j][4 * q + 3] * sr) * sc[3]);
+            *reinterpret_cast<v2i*>(out + (size_t)row * N + c) = pk;
+          }
       }
     }
   }
@@ -283,16 +300,19 @@ hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
   if (swiglu) {
     const long long grid = max_m_tiles * ((N / 2) / 128);
-    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<true, 8>), dim3((unsigned)grid), dim3(kThreads), lds_main<256>() + table,
-                       stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out, status);
+    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<true, 256>), dim3((unsigned)grid), dim3(kThreads),
+                       (lds_main<256>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
+                       status);
   } else if (N % 256 == 0) {
     const long long grid = max_m_tiles * (N / 256);
-    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 8>), dim3((unsigned)grid), dim3(kThreads), lds_main<256>() + table,
-                       stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out, status);
+    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 256>), dim3((unsigned)grid), dim3(kThreads),
+                       (lds_main<256>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
+                       status);
   } else {
     const long long grid = max_m_tiles * (N / 128);
-    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 4>), dim3((unsigned)grid), dim3(kThreads), lds_main<128>() + table,
-                       stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out, status);
+    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 128>), dim3((unsigned)grid), dim3(kThreads),
+                       (lds_main<128>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
+                       status);
   }
   return hipGetLastError();
 }
