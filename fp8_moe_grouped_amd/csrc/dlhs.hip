@@ -14,31 +14,33 @@
 // it enters a bf16 MFMA with f32 accumulation.
 //
 // Tiling (gfx950): a block owns 256 rows x BN output columns of one expert
-// (BN = 256, or 128 when K is not a multiple of 256); four waves own
-// 128 x BN/2 each (256 or 128 f32 accumulators per lane, in AGPRs).  The
-// contraction advances 64 per stage through a ring of LDS stages (three for
-// FP8 codes, two for bf16 weights), each holding
+// (BN = 256, or 128 when K is not a multiple of 256).  Eight waves, two per
+// SIMD, in a 2 x 4 grid own 128 rows x BN/4 columns each (128 f32
+// accumulators per lane); the second wave on a SIMD issues MFMAs while the
+// first waits or converts.  The contraction advances 64 per stage through a
+// three-stage LDS ring (bf16 weights always use BN = 128 to fit), each holding
 //   * the dout tile, [256 rows][64 bf16], 16-byte chunks XOR-swizzled;
 //   * the weight tile in its natural [k][n] layout (n contiguous, which is the
 //     contraction), [BN rows][64 codes] or [BN rows][64 bf16], swizzled;
-//   * per wave, the 64 scales of the stage.
-// Every byte reaches LDS through buffer loads with an LDS destination,
-// issued two stages ahead (codes) so HBM latency hides behind two stages of
-// MFMAs; one barrier per stage, placed before the next stage is first read.
+//   * the 64 scales of the stage (each wave copies eight of them).
+// Every byte reaches LDS through buffer loads with an LDS destination, issued
+// at the top of a stage for two stages ahead; one barrier per stage, just
+// before the next stage is first read.
 //
-// Inner loop: the wave keeps its 128-row dout operand of the stage in
-// registers and streams the weight fragments (16 output columns each): the
-// fragment two ahead is read from LDS, the fragment one ahead is decoded and
-// rounded on the VALU between the 16 MFMAs of the current one.  Each lane
-// reads 16 consecutive contraction values of a row, which the two 16x16x32
-// MFMAs of a stage take as their two 8-value halves; dout and the weight use
-// the same assignment, so the order of summation is the same whether the
-// weights arrive as codes or as bf16 (the bf16 path is the measurement arm
-// and, fed with dequantize_fp8_codes' output, must reproduce the FP8-code
-// result bit for bit).  The MFMA takes the weight as its first operand so
-// each lane owns four consecutive output columns of one row.  Group
-// scheduling and the never-read / never-written stale rows are as in the
-// forward.
+// Inner loop: a wave keeps its 128-row dout operand of the stage in registers
+// and streams its weight fragments (16 output columns each): the next
+// fragment is read from LDS with its 16 scales and decoded, scaled and
+// rounded on the VALU between the 16 MFMAs of the current one; during the
+// last fragment the dout operand of the next stage is reread in place right
+// after the MFMAs that last use each register.  Each lane reads 16 consecutive
+// contraction values of a row, which the two 16x16x32 MFMAs of a stage take
+// as their two 8-value halves; dout and the weight use the same assignment,
+// so the order of summation is the same whether the weights arrive as codes
+// or as bf16 (the bf16 path is the measurement arm and, fed with
+// dequantize_fp8_codes' output, must reproduce the FP8-code result bit for
+// bit).  The MFMA takes the weight as its first operand so each lane owns
+// four consecutive output columns of one row.  Group scheduling and the
+// never-read / never-written stale rows are as in the forward.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -50,22 +52,23 @@ namespace {
 constexpr int BM = 256;
 constexpr int BKN = 64;                 // contraction (n) per stage
 constexpr int kARow = BKN * 2;          // 128 bytes per dout tile row
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;           // 8 waves, two per SIMD
 constexpr int kGroupM = 8;
 
-template <bool FROM_CODES, int NJ>
+template <bool FROM_CODES, int BN>
 struct Cfg {
-  static constexpr int BN = 32 * NJ;                         // output columns per block
+  static constexpr int NJ = BN / 64;                         // 16-column fragments per wave
   static constexpr int kWRow = FROM_CODES ? BKN : BKN * 2;   // bytes per weight tile row
   static constexpr int kABytes = BM * kARow;
   static constexpr int kWBytes = BN * kWRow;
-  static constexpr int kSBytes = FROM_CODES ? 4 * 256 : 0;   // one copy of the 64 scales per wave
+  static constexpr int kSBytes = FROM_CODES ? 256 : 0;       // the stage's 64 scales
   static constexpr int kStage = kABytes + kWBytes + kSBytes;
-  static constexpr int kStages = FROM_CODES ? 3 : 2;
+  static constexpr int kStages = 3;
   static constexpr int kLds = kStages * kStage;
-  static constexpr int kWLoads = kWBytes / (4 * 1024);        // 1 KB wave-wide loads per wave per stage
-  static constexpr int kLoads = 8 + kWLoads + (FROM_CODES ? 1 : 0);
-  static_assert(kLoads < 64, "outstanding loads fit vmcnt");
+  static constexpr int kALoads = kABytes / 1024 / 8;          // 1 KB wave-wide copies per wave per stage
+  static constexpr int kWLoads = kWBytes / 1024 / 8;
+  static constexpr int kLoads = kALoads + kWLoads + (FROM_CODES ? 1 : 0);
+  static_assert(kLoads < 64, "outstanding copies fit vmcnt");
 };
 
 // 16-byte chunk swizzles, conflict-free for the operand reads (16 lanes read
@@ -83,14 +86,14 @@ __device__ __forceinline__ v4i deq8(uint32_t w0, uint32_t w1, const float* sc) {
                (int)pack_bf16x2(c[0] * sc[4], c[1] * sc[5]), (int)pack_bf16x2(d[0] * sc[6], d[1] * sc[7])};
 }
 
-template <bool FROM_CODES, int NJ>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+template <bool FROM_CODES, int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restrict__ codes,
                      const float* __restrict__ wscale, const uint16_t* __restrict__ wbf16,
                      const int* __restrict__ group_sizes, int G, int M, int K, int N,
                      uint16_t* __restrict__ dlhs, int* status) {
-  using C = Cfg<FROM_CODES, NJ>;
-  constexpr int BN = C::BN;
+  using C = Cfg<FROM_CODES, BN>;
+  constexpr int NJ = C::NJ;
   constexpr int S = C::kStages;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* t_start = reinterpret_cast<int*>(smem + C::kLds);
@@ -102,7 +105,7 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;          // 2 x 4 waves
   const int n_tiles = K / BN;
   const int T = t_pre[G];
   const int total = T * n_tiles;
@@ -125,10 +128,10 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   const BufRsrc rw = FROM_CODES ? make_rsrc(codes + (size_t)g * K * N, (uint32_t)K * (uint32_t)N)
                                 : make_rsrc(wbf16 + (size_t)g * K * N, (uint32_t)K * (uint32_t)N * 2u);
   const BufRsrc rs = make_rsrc(FROM_CODES ? wscale + (size_t)g * N : wscale, FROM_CODES ? (uint32_t)N * 4u : 0u);
-  uint32_t va[8];
+  uint32_t va[C::kALoads];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * (8 * wave + j) + (lane >> 3);
+  for (int j = 0; j < C::kALoads; ++j) {
+    const int r = (C::kALoads * wave + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     va[j] = (uint32_t)min(r, rows - 1) * (uint32_t)N * 2u + (uint32_t)(c << 4);
   }
@@ -136,11 +139,11 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
 #pragma unroll
   for (int j = 0; j < C::kWLoads; ++j) {
     if (FROM_CODES) {
-      const int kr = 16 * (C::kWLoads * wave + j) + (lane >> 2);
+      const int kr = (C::kWLoads * wave + j) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((kr >> 2) & 3);
       vw[j] = (uint32_t)(nt * BN + kr) * (uint32_t)N + (uint32_t)(c << 4);
     } else {
-      const int kr = 8 * (C::kWLoads * wave + j) + (lane >> 3);
+      const int kr = (C::kWLoads * wave + j) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ ((kr >> 1) & 7);
       vw[j] = (uint32_t)(nt * BN + kr) * (uint32_t)N * 2u + (uint32_t)(c << 4);
     }
@@ -156,20 +159,21 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   for (int s = 0; s < 2; ++s)
     w_rd[s] = C::kABytes + (FROM_CODES ? w_swz(wn * (16 * NJ) + (lane & 15), q)           // + j * 1024
                                        : a_swz(wn * (16 * NJ) + (lane & 15), 2 * q + s));  // + j * 2048
-  const int s_rd = C::kABytes + C::kWBytes + wave * 256 + q * 64;
+  const int s_rd = C::kABytes + C::kWBytes + q * 64;
 
-  auto issue_stage = [&](int ks) {
-    uint8_t* St = smem + (ks % S) * C::kStage;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(ra, St + (8 * wave + j) * 1024, va[j], (uint32_t)ks * kARow);
-#pragma unroll
-    for (int j = 0; j < C::kWLoads; ++j)
+  // copy number c (0 .. kLoads-1) of stage ks into slot St
+  auto issue_one = [&](uint8_t* St, int ks, int c) {
+    if (c < C::kALoads) {
+      dma16(ra, St + (C::kALoads * wave + c) * 1024, va[c], (uint32_t)ks * kARow);
+    } else if (c < C::kALoads + C::kWLoads) {
+      const int j = c - C::kALoads;
       dma16(rw, St + C::kABytes + (C::kWLoads * wave + j) * 1024, vw[j], (uint32_t)ks * C::kWRow);
-    if (FROM_CODES) dma4(rs, St + C::kABytes + C::kWBytes + wave * 256, (uint32_t)lane * 4u, (uint32_t)ks * 256u);
+    } else if (lane < 8) {     // this wave's eight of the stage's 64 scales
+      dma4(rs, St + C::kABytes + C::kWBytes + wave * 32, (uint32_t)(wave * 8 + lane) * 4u, (uint32_t)ks * 256u);
+    }
   };
-  // weight fragment j of stage ks, as read from LDS (codes: 16 bytes; bf16: 2 x 16 bytes)
-  auto read_w = [&](int ks, int j) {
-    const uint8_t* St = smem + (ks % S) * C::kStage;
+  // weight fragment j as read from LDS (codes: 16 bytes; bf16: 2 x 16 bytes)
+  auto read_w = [&](const uint8_t* St, int j) {
     v8i r;
     if (FROM_CODES) {
       const v4i v = *reinterpret_cast<const v4i*>(St + w_rd[0] + j * 1024);
@@ -181,24 +185,15 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     }
     return r;
   };
-  auto read_scales = [&](int ks, float* sc) {
-    const uint8_t* St = smem + (ks % S) * C::kStage;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const v4f v = *reinterpret_cast<const v4f*>(St + s_rd + 16 * t);
-      sc[4 * t] = v[0]; sc[4 * t + 1] = v[1]; sc[4 * t + 2] = v[2]; sc[4 * t + 3] = v[3];
-    }
-  };
-  auto read_a = [&](int ks, v4i (*a)[2]) {
-    const uint8_t* St = smem + (ks % S) * C::kStage;
-#pragma unroll
-    for (int f = 0; f < 8; ++f)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(St + a_rd[s] + f * 2048);
-  };
   // raw fragment -> the two MFMA operands (halves n = 0..7 and 8..15 of the lane's 16)
-  auto convert = [&](const v8i& r, const float* sc, v4i* w) {
+  auto convert = [&](const uint8_t* St, const v8i& r, v4i* w) {
     if (FROM_CODES) {
+      float sc[16];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v4f v = *reinterpret_cast<const v4f*>(St + s_rd + 16 * t);
+        sc[4 * t] = v[0]; sc[4 * t + 1] = v[1]; sc[4 * t + 2] = v[2]; sc[4 * t + 3] = v[3];
+      }
       w[0] = deq8((uint32_t)r[0], (uint32_t)r[1], sc);
       w[1] = deq8((uint32_t)r[2], (uint32_t)r[3], sc + 8);
     } else {
@@ -214,79 +209,80 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     for (int j = 0; j < NJ; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   const int nk = N / BKN;
+  auto slot = [&](int s) { return smem + (s % S) * C::kStage; };
 
   // ---- prologue: stages 0 .. S-2 in flight, stage 0 landed and its operands in registers
-  issue_stage(0);
-  if (S == 3 && nk > 1) {
-    issue_stage(1);
+#pragma unroll
+  for (int c = 0; c < C::kLoads; ++c) issue_one(slot(0), 0, c);
+  if (nk > 1) {
+#pragma unroll
+    for (int c = 0; c < C::kLoads; ++c) issue_one(slot(1), 1, c);
     wait_vmem_lds<C::kLoads>();
   } else {
     wait_vmem_lds<0>();
   }
   barrier_only();
   v4i a[8][2];
-  read_a(0, a);
-  float sc[16], scn[16];
-  if (FROM_CODES) read_scales(0, sc);
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(slot(0) + a_rd[s] + f * 2048);
   v4i wcur[2];
-  v8i rawn = read_w(0, 1);
-  convert(read_w(0, 0), sc, wcur);
+  convert(slot(0), read_w(slot(0), 0), wcur);
 
-  // One stage.  ISSUE: start the copy of stage ks+S-1; MORE: stage ks+1 exists
-  // (its operands are fetched during the last two weight fragments).
-  auto step = [&](int ks, auto issue_c, auto more_c) {
+  static_assert(S == 3, "the copy slot must differ from the two slots read in a stage");
+  // One stage.  ISSUE: copy stage ks+2 into `wr` (the slot of stage ks-1,
+  // which no wave reads after the previous barrier); MORE: stage ks+1 (slot
+  // `rn`) exists: the barrier before the last fragment makes sure it has
+  // landed, then its first weight fragment and its dout operand are read.
+  // `wr` is distinct from `rd`/`rn`; marking the slots __restrict__ tells the
+  // compiler the reads cannot depend on the copies issued here, so it adds
+  // no wait for them (the explicit wait + barrier order the ring).
+  auto step = [&](int ks, auto issue_c, auto more_c, uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
+                  const uint8_t* __restrict__ rn) {
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr bool MORE = decltype(more_c)::value;
-    if (ISSUE) issue_stage(ks + S - 1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      v8i raw2 = rawn;
-      if (MORE && j == NJ - 2) {
-        // every wave's copy of stage ks+1 has landed (stage ks+2 may still be in flight)
-        if (S == 3 && ISSUE) wait_vmem_lds<C::kLoads>();
+      if (ISSUE) {
+#pragma unroll
+        for (int c = j * C::kLoads / NJ; c < (j + 1) * C::kLoads / NJ; ++c) issue_one(wr, ks + S - 1, c);
+      }
+      if (MORE && j == NJ - 1) {
+        // every wave's copy of stage ks+1 has landed (a copy issued at the
+        // top of this stage may still be in flight)
+        if (ISSUE) wait_vmem_lds<C::kLoads>();
         else wait_vmem_lds<0>();
         barrier_only();
-        if (FROM_CODES) read_scales(ks + 1, scn);
       }
-      if (j + 2 < NJ) raw2 = read_w(ks, j + 2);
-      else if (MORE) raw2 = read_w(ks + 1, j + 2 - NJ);
+      v8i raw;
+      const uint8_t* rs_slot = rd;
+      if (j + 1 < NJ) raw = read_w(rd, j + 1);
+      else if (MORE) { raw = read_w(rn, 0); rs_slot = rn; }
       sched_fence();
-      v4i wnext[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
           acc[f][j] = mfma_bf16_16x16x32(as_bf(wcur[s]), as_bf(a[f][s]), acc[f][j]);
           // last fragment of the stage: a[f][s] is free, refill it from stage ks+1
-          if (MORE && j == NJ - 1) a[f][s] = *reinterpret_cast<const v4i*>(smem + ((ks + 1) % S) * C::kStage +
-                                                                            a_rd[s] + f * 2048);
+          if (MORE && j == NJ - 1) a[f][s] = *reinterpret_cast<const v4i*>(rn + a_rd[s] + f * 2048);
         }
-      if (j + 1 < NJ || MORE) convert(rawn, (j == NJ - 1) ? scn : sc, wnext);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        SCHED_GROUP(0x008, 1);
-        SCHED_GROUP(0x002, 2);
-        if (MORE && j == NJ - 1) SCHED_GROUP(0x100, 1);
-      }
+      v4i wnext[2];
+      if (j + 1 < NJ || MORE) convert(rs_slot, raw, wnext);
       sched_fence();
       wcur[0] = wnext[0];
       wcur[1] = wnext[1];
-      rawn = raw2;
-    }
-    if (FROM_CODES && MORE) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = scn[i];
     }
   };
-
   using T_ = std::true_type;
   using F_ = std::false_type;
   int ks = 0;
-  for (; ks + S - 1 < nk; ++ks) step(ks, T_{}, T_{});      // steady state: copy S-1 ahead
-  if (S == 3 && ks + 1 < nk) step(ks++, F_{}, T_{});       // second to last (three stages)
-  step(ks, F_{}, F_{});                                    // last
+  for (; ks + S - 1 < nk; ++ks) step(ks, T_{}, T_{}, slot(ks + S - 1), slot(ks), slot(ks + 1));
+  if (ks + 1 < nk) { step(ks, F_{}, T_{}, slot(ks + 2), slot(ks), slot(ks + 1)); ++ks; }
+  step(ks, F_{}, F_{}, slot(ks + 2), slot(ks), slot(ks + 1));
 
-  // ---- epilogue: lane owns row f*16 + lane%16, columns cb(j) + 4*(lane/16) + 0..3
+  // ---- epilogue: lane owns row wm*128 + f*16 + lane%16, columns wn*BN/4 + j*16 + 4*(lane/16) + 0..3
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int ml = wm * 128 + f * 16 + (lane & 15);
@@ -310,14 +306,14 @@ hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const fl
   if (M == 0) return hipSuccess;
   const long long max_m_tiles = (M + BM - 1) / BM + G;
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
-  if (K % 256 == 0) {
-    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 8>), dim3((unsigned)(max_m_tiles * (K / 256))), dim3(kThreads),
-                       (Cfg<FROM_CODES, 8>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K, N,
-                       dlhs, status);
+  if (FROM_CODES && K % 256 == 0) {
+    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 256>), dim3((unsigned)(max_m_tiles * (K / 256))), dim3(kThreads),
+                       (Cfg<FROM_CODES, 256>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K,
+                       N, dlhs, status);
   } else {
-    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 4>), dim3((unsigned)(max_m_tiles * (K / 128))), dim3(kThreads),
-                       (Cfg<FROM_CODES, 4>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K, N,
-                       dlhs, status);
+    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 128>), dim3((unsigned)(max_m_tiles * (K / 128))), dim3(kThreads),
+                       (Cfg<FROM_CODES, 128>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K,
+                       N, dlhs, status);
   }
   return hipGetLastError();
 }
