@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
 # were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "c45e9372b952b201", 1811, 78),
-    "wo_gemm": ("gmm_fwd.hip", "c45e9372b952b201", 830, 269),
-    "wi_dlhs": ("dlhs.hip", "c4e03a62b25700e7", 2326, 308),
-    "wo_dlhs": ("dlhs.hip", "c4e03a62b25700e7", 1309, 88),
-    "tgmm": ("tgmm.hip", "f63dced80ce36c0b", 346 + 1836, 374 + 1934),
-    "dequant": ("dequant.hip", "d010579fd4be2bf7", 455, 1083),
+    "wi_gemm": ("gmm_fwd.hip", "0807c470a7e2a627", 2258, 77),
+    "wo_gemm": ("gmm_fwd.hip", "0807c470a7e2a627", 840, 270),
+    "wi_dlhs": ("dlhs.hip", "7ecd4023bd753326", 2289, 269),
+    "wo_dlhs": ("dlhs.hip", "7ecd4023bd753326", 1262, 77),
+    "tgmm": ("tgmm.hip", "60954c8f6c6016d5", 346 + 1450, 188 + 1929),
+    "dequant": ("dequant.hip", "5576245b9a9d9b08", 455, 976),
 }
 
 
