@@ -317,3 +317,108 @@ def tgmm_quant(lhs_bits, dout_bits, group_sizes, grad_fmt: str, tile_m: int = 51
         absum[tl.group] += tile_abs * outer
         sLs[i], sDs[i] = sL, sD
     return TgmmResult(acc.astype(np.float32), acc, absum, tiles, sLs, sDs)
+
+
+# --------------------------------------------------------------------------- dSwiGLU
+
+def dswiglu(dprod: np.ndarray, gate: np.ndarray, up: np.ndarray):
+    """Gradients of ``silu(gate) * up`` with respect to gate and up, given the
+    gradient ``dprod`` of the product, in float64 (P1, Implementation:
+    gmm_dswiglu_fp8 is the wo op whose backward carries the SwiGLU derivative;
+    the derivative itself is calculus on the forward SwiGLU above).
+
+    With sigma(z) = 1 / (1 + exp(-z)) and silu(z) = z * sigma(z):
+    silu'(z) = sigma(z) + z * sigma(z) * (1 - sigma(z)), so
+    ``d_gate = dprod * up * silu'(gate)`` and ``d_up = dprod * silu(gate)``.
+    """
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-gate))
+    dsilu = sig * (1.0 + gate * (1.0 - sig))
+    return dprod * up * dsilu, dprod * gate * sig
+
+
+@dataclass
+class DswigluResult:
+    rows: np.ndarray
+    group: np.ndarray
+    dh: np.ndarray       # f64 wo dLHS before any rounding [R, I]
+    dh_absum: np.ndarray # sum_n |dout * w|   [R, I]
+    y: np.ndarray        # f64 [R, 2I]: [d_gate | d_up] before the bf16 rounding
+    out: np.ndarray      # bf16 bits [R, 2I]
+
+
+def gmm_dswiglu(dout_bits, codes, scale, group_sizes, preact_bits, *, rows=None) -> DswigluResult:
+    """wo backward dLHS with the SwiGLU derivative fused after it (P1,
+    Implementation: gmm_dswiglu_fp8 for wo; _run_wo_gmm_dswiglu).
+
+    ``codes``/``scale`` are the wo weight ``[G, I, H]``; ``dout`` is the wo
+    output gradient ``[M, H]``; ``preact`` is the wi pre-activation
+    ``[M, 2I]`` (bf16, ``[gate | up]``) kept by the forward.  The wo dLHS
+    ``dh = dout @ dequantize(codes, scale)^T`` stays unrounded (float64 here)
+    and only the two gradients are rounded to bf16:
+    ``out = bf16([dh * up * silu'(gate) | dh * silu(gate)])``.
+    """
+    preact_bits = np.asarray(preact_bits)
+    G, I, H = codes.shape
+    M = np.asarray(dout_bits).shape[0]
+    assert preact_bits.shape == (M, 2 * I)
+    dl = gmm_dlhs(dout_bits, codes, scale, group_sizes, rows=rows)
+    z = F.bf16_to_f64(preact_bits[dl.rows])
+    dg, du = dswiglu(dl.y, z[:, :I], z[:, I:])
+    y = np.concatenate([dg, du], axis=1)
+    return DswigluResult(dl.rows, dl.group, dl.y, dl.absum, y, F.f64_to_bf16_bits(y))
+
+
+# --------------------------------------------------------------------------- MoE FFN
+
+#: bf16 NaN written to buffer rows an op does not produce (never read)
+_STALE_BF16 = np.uint16(0x7FC0)
+
+
+def _full_rows(valid_bits: np.ndarray, M: int) -> np.ndarray:
+    out = np.full((M, valid_bits.shape[1]), _STALE_BF16, dtype=np.uint16)
+    out[:valid_bits.shape[0]] = valid_bits
+    return out
+
+
+@dataclass
+class FfnResult:
+    fwd_wi: FwdResult          # wi forward with SwiGLU (out = h, y = pre-activation)
+    preact: np.ndarray         # bf16 bits [Mv, 2I]: the pre-activation the backward reads
+    h: np.ndarray              # bf16 bits [Mv, I]
+    fwd_wo: FwdResult          # wo forward (out = y)
+    dsw: DswigluResult         # wo dLHS + dSwiGLU (out = d preact)
+    dx: DlhsResult             # wi dLHS (out = dx)
+    dwo: TgmmResult            # [G, I, H]
+    dwi: TgmmResult            # [G, H, 2I]
+
+
+def moe_ffn(x_bits, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes, dy_bits, grad_fmt: str,
+            tile_m: int = 512) -> FfnResult:
+    """Forward and backward of one routed-expert FFN on a static ragged buffer
+    (P1, Implementation: gmm_up_or_silu runs gmm_silu_fp8 for wi and
+    _run_wo_gmm_dswiglu runs gmm_dswiglu_fp8 for wo; P3, What: both weight
+    gradients are tgmm with in-kernel operand quantization).
+
+    x ``[M, H]``, wi ``[G, H, 2I]``, wo ``[G, I, H]``, dy ``[M, H]`` (the
+    gradient of the FFN output).  Steps, each an oracle op above:
+      1. wi forward with SwiGLU: h = bf16(silu(gate) * up); the pre-activation
+         [gate | up] is kept as bf16 for the backward;
+      2. wo forward: y = gmm_fwd(h, wo);
+      3. wo dLHS + dSwiGLU: d_preact = gmm_dswiglu(dy, wo, preact);
+      4. wi dLHS: dx = gmm_dlhs(d_preact, wi);
+      5. weight gradients: dwo = tgmm(h, dy), dwi = tgmm(x, d_preact).
+    """
+    x_bits = np.asarray(x_bits)
+    M = x_bits.shape[0]
+    fwd_wi = gmm_fwd(x_bits, wi_codes, wi_scale, group_sizes, swiglu_out=True)
+    preact = F.f64_to_bf16_bits(fwd_wi.y)
+    h = fwd_wi.out
+    h_full = _full_rows(h, M)
+    fwd_wo = gmm_fwd(h_full, wo_codes, wo_scale, group_sizes)
+    dsw = gmm_dswiglu(dy_bits, wo_codes, wo_scale, group_sizes, _full_rows(preact, M))
+    dz_full = _full_rows(dsw.out, M)
+    dx = gmm_dlhs(dz_full, wi_codes, wi_scale, group_sizes)
+    dwo = tgmm_quant(h_full, dy_bits, group_sizes, grad_fmt, tile_m)
+    dwi = tgmm_quant(x_bits, dz_full, group_sizes, grad_fmt, tile_m)
+    return FfnResult(fwd_wi, preact, h, fwd_wo, dsw, dx, dwo, dwi)

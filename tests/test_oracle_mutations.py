@@ -5,6 +5,7 @@ import pytest
 
 from oracle import formats as F
 from oracle import gmm as O
+from tests import test_oracle_dswiglu as TD
 from tests import test_oracle_formats as TF
 from tests import test_oracle_gmm as TG
 
@@ -28,6 +29,10 @@ PINS = [
     TF.test_encode_specials,
     lambda: TF.test_encode_roundtrip_all_finite_codes(F.E4M3),
     TF.test_bf16_specials,
+    TD.test_dswiglu_matches_autograd_and_finite_differences,
+    TD.test_dswiglu_closed_forms,
+    TD.test_gmm_dswiglu_is_gradient_of_wo_loss,
+    lambda: TD.test_moe_ffn_matches_straight_through_gradient(F.E4M3),
 ]
 
 
@@ -81,6 +86,24 @@ _real_tiles = O.tgmm_tiles
 _real_col_scales = O.column_scales
 _real_fwd_rows = O._fwd_rows
 _real_dequant = O.dequantize
+_real_dswiglu = O.dswiglu
+_real_gmm_dswiglu = O.gmm_dswiglu
+
+
+def _mut_dswiglu_sigma_only(d, g, u):
+    sig = 1.0 / (1.0 + np.exp(-np.clip(g, -700, 700)))
+    return d * u * sig, d * g * sig
+
+
+def _mut_dswiglu_outputs_swapped(d, g, u):
+    dg, du = _real_dswiglu(d, g, u)
+    return du, dg
+
+
+def _mut_dswiglu_preact_halves_swapped(dout, codes, scale, gs, preact, rows=None):
+    p = np.asarray(preact)
+    I = p.shape[1] // 2
+    return _real_gmm_dswiglu(dout, codes, scale, gs, np.concatenate([p[:, I:], p[:, :I]], axis=1), rows=rows)
 
 
 def _mut_tiles_group_aligned(gs, M, tile_m):
@@ -129,6 +152,10 @@ MUTATIONS = {
     "weight scale of channel 0 only": (O, "_fwd_rows", _mut_scale_first_channel),
     "dequant product in f64": (O, "dequantize", _mut_dequant_f64_product),
     "bf16 rounding truncates": (F, "round_to_bf16", _mut_bf16_truncate),
+    "dswiglu drops the z sigma (1 - sigma) term": (O, "dswiglu", _mut_dswiglu_sigma_only),
+    "dswiglu gate and up gradients swapped": (O, "dswiglu", _mut_dswiglu_outputs_swapped),
+    "dswiglu reads the pre-activation halves swapped": (O, "gmm_dswiglu", _mut_dswiglu_preact_halves_swapped),
+    "dswiglu sign flipped": (O, "dswiglu", lambda d, g, u: tuple(-v for v in _real_dswiglu(d, g, u))),
 }
 
 
