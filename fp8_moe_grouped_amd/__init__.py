@@ -26,7 +26,7 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
 DEV_SUM_CLAMPED, DEV_NEGATIVE_SIZE = 1, 2
 E4M3, E5M2 = 0, 1
-OP_FWD, OP_SILU, OP_DLHS, OP_TGMM, OP_BF16_FWD, OP_BF16_DLHS = 0, 1, 2, 3, 4, 5
+OP_FWD, OP_SILU, OP_DLHS, OP_TGMM, OP_BF16_FWD, OP_BF16_DLHS, OP_FFN_FWD, OP_FFN_BWD = 0, 1, 2, 3, 4, 5, 6, 7
 GRAD_DTYPES = {"e4m3": E4M3, "e5m2": E5M2}
 
 
@@ -45,13 +45,17 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "gmm_fp8_fwd": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P, _P],
-    "gmm_silu_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P, _P],
+    "gmm_silu_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P],
     "gmm_dlhs_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _SZ, _P, _P],
     "tgmm_quant": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P],
     "dequantize_fp8_codes": [_P, _P, _I32, _I64, _I64, _P, _P],
     "quantize_rows_fp8": [_P, _P, _I64, _I64, _I32, _P, _P, _P],
     "gmm_fp8_fwd_q": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
-    "gmm_silu_fp8_q": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
+    "gmm_silu_fp8_q": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P],
+    "gmm_dswiglu_fp8": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
+    "moe_ffn_fp8_fwd": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P, _P],
+    "moe_ffn_fp8_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P,
+                        _SZ, _P, _P],
     "gmm_bf16_fwd": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
     "gmm_bf16_dlhs": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
 }
@@ -138,7 +142,7 @@ def _workspace(op, M, K, N, G, dev, tile_m=512, workspace=None):
     return workspace, need
 
 
-def _fwd(name, op, lhs, codes, scale, group_sizes, out, debug, dev_status, workspace, swiglu):
+def _fwd(name, op, lhs, codes, scale, group_sizes, out, debug, dev_status, workspace, swiglu, preact=None):
     _req(lhs, "lhs", torch.bfloat16, 2)
     _req(codes, "codes", torch.uint8, 3)
     _req(scale, "scale", torch.float32, 2)
@@ -153,13 +157,21 @@ def _fwd(name, op, lhs, codes, scale, group_sizes, out, debug, dev_status, works
     if out is None:
         out = torch.empty((M, ncol), dtype=torch.bfloat16, device=dev)
     _req(out, "out", torch.bfloat16, 2)
+    if preact is True:
+        preact = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if preact is not None:
+        _req(preact, "preact", torch.bfloat16, 2)
+        if tuple(preact.shape) != (M, N):
+            raise ValueError(f"preact must be [{M}, {N}], got {tuple(preact.shape)}")
     dbg_codes = torch.empty((M, K), dtype=torch.uint8, device=dev) if debug else None
     dbg_scale = torch.empty((M,), dtype=torch.float32, device=dev) if debug else None
     ws, need = _workspace(op, M, K, N, G, dev, workspace=workspace)
+    extra = (_ptr(preact),) if swiglu else ()
     with torch.cuda.device(dev):
-        _call(name, _ptr(lhs), _ptr(codes), _ptr(scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
+        _call(name, _ptr(lhs), _ptr(codes), _ptr(scale), _ptr(group_sizes), M, K, N, G, _ptr(out), *extra,
               _ptr(dbg_codes), _ptr(dbg_scale), _ptr(ws), need, _ptr(dev_status), _stream(dev))
-    return (out, dbg_codes, dbg_scale) if debug else out
+    res = (out,) + ((preact,) if preact is not None else ()) + ((dbg_codes, dbg_scale) if debug else ())
+    return res if len(res) > 1 else out
 
 
 def gmm_fp8_fwd(lhs, codes, scale, group_sizes, *, out=None, debug=False, dev_status=None, workspace=None):
@@ -168,9 +180,14 @@ def gmm_fp8_fwd(lhs, codes, scale, group_sizes, *, out=None, debug=False, dev_st
     return _fwd("gmm_fp8_fwd", OP_FWD, lhs, codes, scale, group_sizes, out, debug, dev_status, workspace, False)
 
 
-def gmm_silu_fp8(lhs, codes, scale, group_sizes, *, out=None, debug=False, dev_status=None, workspace=None):
-    """Native FP8 forward GMM with fused SwiGLU over [gate | up]; bf16 [M, N/2]."""
-    return _fwd("gmm_silu_fp8", OP_SILU, lhs, codes, scale, group_sizes, out, debug, dev_status, workspace, True)
+def gmm_silu_fp8(lhs, codes, scale, group_sizes, *, out=None, preact=None, debug=False, dev_status=None,
+                 workspace=None):
+    """Native FP8 forward GMM with fused SwiGLU over [gate | up]; bf16 [M, N/2].
+    ``preact`` (a bf16 [M, N] tensor, or True to allocate one) also receives
+    the pre-activation; the result is then ``(out, preact)`` (followed by the
+    debug outputs when asked)."""
+    return _fwd("gmm_silu_fp8", OP_SILU, lhs, codes, scale, group_sizes, out, debug, dev_status, workspace, True,
+                preact)
 
 
 def quantize_rows_fp8(lhs, group_sizes, *, codes=None, scales=None):
@@ -192,7 +209,7 @@ def quantize_rows_fp8(lhs, group_sizes, *, codes=None, scales=None):
     return codes, scales
 
 
-def _fwd_q(name, aq, ascale, codes, scale, group_sizes, out, dev_status, swiglu):
+def _fwd_q(name, aq, ascale, codes, scale, group_sizes, out, dev_status, swiglu, preact=None):
     _req(aq, "aq", torch.uint8, 2)
     _req(ascale, "ascale", torch.float32, 1)
     _req(codes, "codes", torch.uint8, 3)
@@ -206,9 +223,14 @@ def _fwd_q(name, aq, ascale, codes, scale, group_sizes, out, dev_status, swiglu)
     if out is None:
         out = torch.empty((M, N // 2 if swiglu else N), dtype=torch.bfloat16, device=dev)
     _req(out, "out", torch.bfloat16, 2)
+    if preact is not None:
+        _req(preact, "preact", torch.bfloat16, 2)
+        if tuple(preact.shape) != (M, N):
+            raise ValueError(f"preact must be [{M}, {N}], got {tuple(preact.shape)}")
+    extra = (_ptr(preact),) if swiglu else ()
     with torch.cuda.device(dev):
         _call(name, _ptr(aq), _ptr(ascale), _ptr(codes), _ptr(scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
-              _ptr(dev_status), _stream(dev))
+              *extra, _ptr(dev_status), _stream(dev))
     return out
 
 
@@ -217,9 +239,10 @@ def gmm_fp8_fwd_q(aq, ascale, codes, scale, group_sizes, *, out=None, dev_status
     return _fwd_q("gmm_fp8_fwd_q", aq, ascale, codes, scale, group_sizes, out, dev_status, False)
 
 
-def gmm_silu_fp8_q(aq, ascale, codes, scale, group_sizes, *, out=None, dev_status=None):
-    """FP8 forward GEMM + SwiGLU on already quantized activations."""
-    return _fwd_q("gmm_silu_fp8_q", aq, ascale, codes, scale, group_sizes, out, dev_status, True)
+def gmm_silu_fp8_q(aq, ascale, codes, scale, group_sizes, *, out=None, preact=None, dev_status=None):
+    """FP8 forward GEMM + SwiGLU on already quantized activations; a bf16
+    [M, N] ``preact`` tensor, if given, receives the pre-activation."""
+    return _fwd_q("gmm_silu_fp8_q", aq, ascale, codes, scale, group_sizes, out, dev_status, True, preact)
 
 
 def gmm_dlhs_fp8(dout, codes, scale, group_sizes, *, out=None, dev_status=None, workspace=None):
@@ -241,6 +264,99 @@ def gmm_dlhs_fp8(dout, codes, scale, group_sizes, *, out=None, dev_status=None, 
         _call("gmm_dlhs_fp8", _ptr(dout), _ptr(codes), _ptr(scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
               _ptr(ws), need, _ptr(dev_status), _stream(dev))
     return out
+
+
+def gmm_dswiglu_fp8(dout, codes, scale, group_sizes, preact, *, out=None, dev_status=None):
+    """wo backward dLHS fused with the SwiGLU derivative: from the wo output
+    gradient dout [M, H], the wo codes [G, I, H] and the wi pre-activation
+    preact [M, 2I], returns the pre-activation gradient bf16 [M, 2I]."""
+    _req(dout, "dout", torch.bfloat16, 2)
+    _req(codes, "codes", torch.uint8, 3)
+    _req(scale, "scale", torch.float32, 2)
+    _req(group_sizes, "group_sizes", torch.int32, 1)
+    _req(preact, "preact", torch.bfloat16, 2)
+    dev = _same_device(dout, codes, scale, group_sizes, preact)
+    M, N = dout.shape
+    G, K, N2 = codes.shape
+    if N2 != N or tuple(scale.shape) != (G, N) or group_sizes.shape[0] != G or tuple(preact.shape) != (M, 2 * K):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M, 2 * K), dtype=torch.bfloat16, device=dev)
+    _req(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, 2 * K):
+        raise ValueError("out must be [M, 2K]")
+    with torch.cuda.device(dev):
+        _call("gmm_dswiglu_fp8", _ptr(dout), _ptr(codes), _ptr(scale), _ptr(group_sizes), _ptr(preact), M, K, N, G,
+              _ptr(out), _ptr(dev_status), _stream(dev))
+    return out
+
+
+def _ffn_shapes(x, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes):
+    _req(x, "x", torch.bfloat16, 2)
+    _req(wi_codes, "wi_codes", torch.uint8, 3)
+    _req(wi_scale, "wi_scale", torch.float32, 2)
+    _req(wo_codes, "wo_codes", torch.uint8, 3)
+    _req(wo_scale, "wo_scale", torch.float32, 2)
+    _req(group_sizes, "group_sizes", torch.int32, 1)
+    dev = _same_device(x, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes)
+    M, H = x.shape
+    G, H2, I2 = wi_codes.shape
+    I = I2 // 2
+    if (H2 != H or I2 != 2 * I or tuple(wi_scale.shape) != (G, I2) or tuple(wo_codes.shape) != (G, I, H)
+            or tuple(wo_scale.shape) != (G, H) or group_sizes.shape[0] != G):
+        raise ValueError(f"FFN shape mismatch: x {tuple(x.shape)} wi {tuple(wi_codes.shape)} "
+                         f"wo {tuple(wo_codes.shape)}")
+    return dev, M, H, I, G
+
+
+def _out(t, shape, dtype, dev, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _req(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def moe_ffn_fp8_fwd(x, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes, *, keep_preact=True, h=None,
+                    preact=None, y=None, dev_status=None, workspace=None):
+    """Forward of one routed-expert FFN: h = SwiGLU FP8 GMM of x with wi,
+    y = FP8 GMM of h with wo.  Returns (y [M, H], h [M, I], preact [M, 2I] or
+    None)."""
+    dev, M, H, I, G = _ffn_shapes(x, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes)
+    h = _out(h, (M, I), torch.bfloat16, dev, "h")
+    y = _out(y, (M, H), torch.bfloat16, dev, "y")
+    preact = _out(preact, (M, 2 * I), torch.bfloat16, dev, "preact") if (keep_preact or preact is not None) else None
+    ws, need = _workspace(OP_FFN_FWD, M, H, I, G, dev, tile_m=0, workspace=workspace)
+    with torch.cuda.device(dev):
+        _call("moe_ffn_fp8_fwd", _ptr(x), _ptr(wi_codes), _ptr(wi_scale), _ptr(wo_codes), _ptr(wo_scale),
+              _ptr(group_sizes), M, H, I, G, _ptr(h), _ptr(preact), _ptr(y), _ptr(ws), need, _ptr(dev_status),
+              _stream(dev))
+    return y, h, preact
+
+
+def moe_ffn_fp8_bwd(x, h, preact, dy, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes, grad_dtype="e5m2", *,
+                    need_dx=True, d_preact=None, dx=None, dwi=None, dwo=None, dev_status=None, workspace=None):
+    """Backward of one routed-expert FFN from the forward's x, h, preact and
+    the output gradient dy [M, H].  Returns (dx [M, H] or None, dwi
+    [G, H, 2I] f32, dwo [G, I, H] f32, d_preact [M, 2I])."""
+    dev, M, H, I, G = _ffn_shapes(x, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes)
+    for t, name, shape in ((h, "h", (M, I)), (preact, "preact", (M, 2 * I)), (dy, "dy", (M, H))):
+        _req(t, name, torch.bfloat16, 2)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
+    _same_device(x, h, preact, dy)
+    gd = GRAD_DTYPES[grad_dtype] if isinstance(grad_dtype, str) else int(grad_dtype)
+    d_preact = _out(d_preact, (M, 2 * I), torch.bfloat16, dev, "d_preact")
+    dx = _out(dx, (M, H), torch.bfloat16, dev, "dx") if (need_dx or dx is not None) else None
+    dwi = _out(dwi, (G, H, 2 * I), torch.float32, dev, "dwi")
+    dwo = _out(dwo, (G, I, H), torch.float32, dev, "dwo")
+    ws, need = _workspace(OP_FFN_BWD, M, H, I, G, dev, tile_m=512, workspace=workspace)
+    with torch.cuda.device(dev):
+        _call("moe_ffn_fp8_bwd", _ptr(x), _ptr(h), _ptr(preact), _ptr(dy), _ptr(wi_codes), _ptr(wi_scale),
+              _ptr(wo_codes), _ptr(wo_scale), _ptr(group_sizes), M, H, I, G, gd, _ptr(d_preact), _ptr(dx),
+              _ptr(dwi), _ptr(dwo), _ptr(ws), need, _ptr(dev_status), _stream(dev))
+    return dx, dwi, dwo, d_preact
 
 
 def tgmm_quant(lhs, dout, group_sizes, grad_dtype="e5m2", tile_m=512, *, out=None, debug=False,

@@ -27,15 +27,15 @@ int check_common(int64_t M, int64_t K, int64_t N, int32_t G) {
 size_t fwd_ws(int64_t M, int64_t K) { return align_up((size_t)M * K) + align_up((size_t)M * 4); }
 
 int fwd_common(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
-               int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale, void* ws,
-               size_t ws_bytes, int32_t* dev_status, void* stream, bool swiglu) {
+               int64_t K, int64_t N, int32_t G, void* out, void* preact, uint8_t* dbg_codes, float* dbg_scale,
+               void* ws, size_t ws_bytes, int32_t* dev_status, void* stream, bool swiglu) {
   if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
   int st = check_common(M, K, N, G);
   if (st != FP8GMM_OK) return st;
   if (M > 0 && (!lhs || !out)) return FP8GMM_ERR_NULL;
   if (K > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
   if (swiglu && ((N / 2) % 128 != 0)) return FP8GMM_ERR_UNSUPPORTED;
-  if (!aligned16(lhs) || !aligned16(codes) || !aligned16(scale) || !aligned16(out) ||
+  if (!aligned16(lhs) || !aligned16(codes) || !aligned16(scale) || !aligned16(out) || !aligned16(preact) ||
       (dbg_codes && !aligned16(dbg_codes)))
     return FP8GMM_ERR_ALIGN;   // NULL (M == 0) counts as aligned
   const size_t need = fwd_ws(M, K);
@@ -48,7 +48,7 @@ int fwd_common(const void* lhs, const uint8_t* codes, const float* scale, const 
       hipSuccess)
     return FP8GMM_ERR_HIP;
   if (launch_gmm_fp8_fwd(aq, as, codes, scale, group_sizes, G, (int)M, (int)K, (int)N, swiglu,
-                         static_cast<uint16_t*>(out), dev_status, s) != hipSuccess)
+                         static_cast<uint16_t*>(out), static_cast<uint16_t*>(preact), dev_status, s) != hipSuccess)
     return FP8GMM_ERR_HIP;
   return FP8GMM_OK;
 }
@@ -60,15 +60,15 @@ extern "C" {
 int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
                 int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale, void* ws,
                 size_t ws_bytes, int32_t* dev_status, void* stream) {
-  return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, dbg_codes, dbg_scale, ws, ws_bytes, dev_status,
-                    stream, false);
+  return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, nullptr, dbg_codes, dbg_scale, ws, ws_bytes,
+                    dev_status, stream, false);
 }
 
 int gmm_silu_fp8(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
-                 int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale, void* ws,
-                 size_t ws_bytes, int32_t* dev_status, void* stream) {
-  return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, dbg_codes, dbg_scale, ws, ws_bytes, dev_status,
-                    stream, true);
+                 int64_t K, int64_t N, int32_t G, void* out, void* preact, uint8_t* dbg_codes, float* dbg_scale,
+                 void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, preact, dbg_codes, dbg_scale, ws, ws_bytes,
+                    dev_status, stream, true);
 }
 
 int quantize_rows_fp8(const void* lhs, const int32_t* group_sizes, int64_t M, int64_t K, int32_t G,
@@ -87,17 +87,18 @@ int quantize_rows_fp8(const void* lhs, const int32_t* group_sizes, int64_t M, in
 
 static int fwd_q_common(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
                         const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
-                        int32_t* dev_status, void* stream, bool swiglu) {
+                        void* preact, int32_t* dev_status, void* stream, bool swiglu) {
   if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
   int st = check_common(M, K, N, G);
   if (st != FP8GMM_OK) return st;
   if (M > 0 && (!aq || !ascale || !out)) return FP8GMM_ERR_NULL;
   if (swiglu && ((N / 2) % 128 != 0)) return FP8GMM_ERR_UNSUPPORTED;
-  if (!aligned16(aq) || !aligned16(codes) || !aligned16(scale) || !aligned16(out)) return FP8GMM_ERR_ALIGN;
+  if (!aligned16(aq) || !aligned16(codes) || !aligned16(scale) || !aligned16(out) || !aligned16(preact))
+    return FP8GMM_ERR_ALIGN;
   if (M == 0) return FP8GMM_OK;
   if (launch_gmm_fp8_fwd(aq, ascale, codes, scale, group_sizes, G, (int)M, (int)K, (int)N, swiglu,
-                         static_cast<uint16_t*>(out), dev_status, reinterpret_cast<hipStream_t>(stream)) !=
-      hipSuccess)
+                         static_cast<uint16_t*>(out), static_cast<uint16_t*>(preact), dev_status,
+                         reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return FP8GMM_ERR_HIP;
   return FP8GMM_OK;
 }
@@ -105,13 +106,13 @@ static int fwd_q_common(const uint8_t* aq, const float* ascale, const uint8_t* c
 int gmm_fp8_fwd_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
                   int32_t* dev_status, void* stream) {
-  return fwd_q_common(aq, ascale, codes, scale, group_sizes, M, K, N, G, out, dev_status, stream, false);
+  return fwd_q_common(aq, ascale, codes, scale, group_sizes, M, K, N, G, out, nullptr, dev_status, stream, false);
 }
 
 int gmm_silu_fp8_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
-                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
+                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out, void* preact,
                    int32_t* dev_status, void* stream) {
-  return fwd_q_common(aq, ascale, codes, scale, group_sizes, M, K, N, G, out, dev_status, stream, true);
+  return fwd_q_common(aq, ascale, codes, scale, group_sizes, M, K, N, G, out, preact, dev_status, stream, true);
 }
 
 int dequantize_fp8_codes(const uint8_t* codes, const float* scale, int32_t G, int64_t K, int64_t N, void* out,
@@ -166,6 +167,23 @@ int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, in
   return FP8GMM_OK;
 }
 
+int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                    const void* preact, int64_t M, int64_t K, int64_t N, int32_t G, void* d_preact,
+                    int32_t* dev_status, void* stream) {
+  if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!dout || !preact || !d_preact)) return FP8GMM_ERR_NULL;
+  if (!aligned16(dout) || !aligned16(codes) || !aligned16(scale) || !aligned16(preact) || !aligned16(d_preact))
+    return FP8GMM_ERR_ALIGN;
+  if (M == 0) return FP8GMM_OK;
+  if (launch_gmm_dswiglu_fp8(static_cast<const uint16_t*>(dout), codes, scale, group_sizes, G, (int)M, (int)K,
+                             (int)N, static_cast<const uint16_t*>(preact), static_cast<uint16_t*>(d_preact),
+                             dev_status, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
 int gmm_bf16_fwd(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
                  int32_t G, void* out, int32_t* dev_status, void* stream) {
   if (!w || !group_sizes) return FP8GMM_ERR_NULL;
@@ -196,6 +214,89 @@ int gmm_bf16_dlhs(const void* dout, const void* w, const int32_t* group_sizes, i
   return FP8GMM_OK;
 }
 
+// Shapes of one FFN: x [M, H], wi [G, H, 2I], wo [G, I, H].
+static int check_ffn(int64_t M, int64_t H, int64_t I, int32_t G) {
+  if (H <= 0 || I <= 0) return FP8GMM_ERR_SHAPE;
+  int st = check_common(M, H, 2 * I, G);
+  if (st != FP8GMM_OK) return st;
+  st = check_common(M, I, H, G);
+  if (st != FP8GMM_OK) return st;
+  if (H % 256 != 0 || I % 256 != 0 || H > kMaxK || I > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
+  return FP8GMM_OK;
+}
+
+static size_t ffn_fwd_ws(int64_t M, int64_t H, int64_t I) { return fwd_ws(M, H > I ? H : I); }
+
+static size_t ffn_bwd_ws(int64_t M, int64_t H, int64_t I, int32_t G) {
+  const size_t a = tgmm_workspace_bytes(M, I, H, G), b = tgmm_workspace_bytes(M, H, 2 * I, G);
+  return a > b ? a : b;
+}
+
+int moe_ffn_fp8_fwd(const void* x, const uint8_t* wi_codes, const float* wi_scale, const uint8_t* wo_codes,
+                    const float* wo_scale, const int32_t* group_sizes, int64_t M, int64_t H, int64_t I, int32_t G,
+                    void* h, void* preact, void* y, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  if (!wi_codes || !wi_scale || !wo_codes || !wo_scale || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_ffn(M, H, I, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!x || !h || !y)) return FP8GMM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wi_codes) || !aligned16(wi_scale) || !aligned16(wo_codes) ||
+      !aligned16(wo_scale) || !aligned16(h) || !aligned16(preact) || !aligned16(y))
+    return FP8GMM_ERR_ALIGN;
+  const size_t need = ffn_fwd_ws(M, H, I);
+  if (M > 0 && (!ws || ws_bytes < need)) return FP8GMM_ERR_WORKSPACE;
+  if (M == 0) return FP8GMM_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // the two activation quantizations share the workspace (stream order)
+  uint8_t* aq = static_cast<uint8_t*>(ws);
+  float* as = reinterpret_cast<float*>(aq + align_up((size_t)M * (size_t)(H > I ? H : I)));
+  if (launch_quant_rows_e4m3(static_cast<const uint16_t*>(x), group_sizes, G, (int)M, (int)H, aq, as, s) !=
+          hipSuccess ||
+      launch_gmm_fp8_fwd(aq, as, wi_codes, wi_scale, group_sizes, G, (int)M, (int)H, (int)(2 * I), true,
+                         static_cast<uint16_t*>(h), static_cast<uint16_t*>(preact), dev_status, s) != hipSuccess ||
+      launch_quant_rows_e4m3(static_cast<const uint16_t*>(h), group_sizes, G, (int)M, (int)I, aq, as, s) !=
+          hipSuccess ||
+      launch_gmm_fp8_fwd(aq, as, wo_codes, wo_scale, group_sizes, G, (int)M, (int)I, (int)H, false,
+                         static_cast<uint16_t*>(y), nullptr, dev_status, s) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
+int moe_ffn_fp8_bwd(const void* x, const void* h, const void* preact, const void* dy, const uint8_t* wi_codes,
+                    const float* wi_scale, const uint8_t* wo_codes, const float* wo_scale,
+                    const int32_t* group_sizes, int64_t M, int64_t H, int64_t I, int32_t G, int32_t grad_dtype,
+                    void* d_preact, void* dx, float* dwi, float* dwo, void* ws, size_t ws_bytes,
+                    int32_t* dev_status, void* stream) {
+  if (!wi_codes || !wi_scale || !wo_codes || !wo_scale || !group_sizes || !dwi || !dwo) return FP8GMM_ERR_NULL;
+  int st = check_ffn(M, H, I, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!x || !h || !preact || !dy || !d_preact)) return FP8GMM_ERR_NULL;
+  if (grad_dtype != FP8GMM_E4M3 && grad_dtype != FP8GMM_E5M2) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(h) || !aligned16(preact) || !aligned16(dy) || !aligned16(wi_codes) ||
+      !aligned16(wi_scale) || !aligned16(wo_codes) || !aligned16(wo_scale) || !aligned16(d_preact) ||
+      !aligned16(dx) || !aligned16(dwi) || !aligned16(dwo))
+    return FP8GMM_ERR_ALIGN;
+  const size_t need = ffn_bwd_ws(M, H, I, G);
+  if (need > 0 && (!ws || ws_bytes < need)) return FP8GMM_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool e5m2 = grad_dtype == FP8GMM_E5M2;
+  uint16_t* dz = static_cast<uint16_t*>(d_preact);
+  if (M > 0) {
+    if (launch_gmm_dswiglu_fp8(static_cast<const uint16_t*>(dy), wo_codes, wo_scale, group_sizes, G, (int)M, (int)I,
+                               (int)H, static_cast<const uint16_t*>(preact), dz, dev_status, s) != hipSuccess)
+      return FP8GMM_ERR_HIP;
+    if (dx && launch_gmm_dlhs_fp8(dz, wi_codes, wi_scale, group_sizes, G, (int)M, (int)H, (int)(2 * I),
+                                  static_cast<uint16_t*>(dx), dev_status, s) != hipSuccess)
+      return FP8GMM_ERR_HIP;
+  }
+  // weight gradients (written fully, zeros for experts without rows)
+  if (launch_tgmm_quant(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(dy), group_sizes, G, (int)M,
+                        (int)I, (int)H, e5m2, dwo, nullptr, nullptr, ws, dev_status, s) != hipSuccess ||
+      launch_tgmm_quant(static_cast<const uint16_t*>(x), dz, group_sizes, G, (int)M, (int)H, (int)(2 * I), e5m2, dwi,
+                        nullptr, nullptr, ws, dev_status, s) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
 size_t fp8gmm_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t G, int32_t tile_m) {
   if (check_common(M, K, N, G) != FP8GMM_OK) return 0;
   switch (op) {
@@ -204,6 +305,10 @@ size_t fp8gmm_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32
       return fwd_ws(M, K);
     case FP8GMM_OP_TGMM:
       return (tile_m == 512 && K % 256 == 0) ? tgmm_workspace_bytes(M, K, N, G) : 0;
+    case FP8GMM_OP_FFN_FWD:
+      return check_ffn(M, K, N, G) == FP8GMM_OK ? ffn_fwd_ws(M, K, N) : 0;
+    case FP8GMM_OP_FFN_BWD:
+      return (tile_m == 512 && check_ffn(M, K, N, G) == FP8GMM_OK) ? ffn_bwd_ws(M, K, N, G) : 0;
     default:
       return 0;
   }

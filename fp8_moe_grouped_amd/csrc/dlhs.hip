@@ -41,6 +41,14 @@
 // bit).  The MFMA takes the weight as its first operand so each lane owns
 // four consecutive output columns of one row.  Group scheduling and the
 // never-read / never-written stale rows are as in the forward.
+//
+// dSwiGLU arm (the backward of the wo op gmm_dswiglu_fp8, "MoE: native FP8
+// QAT for routed-expert GMMs", Implementation: _run_wo_gmm_dswiglu): the
+// dLHS of wo is the gradient dh of h = silu(gate) * up, and the epilogue turns
+// it into the gradient of the wi pre-activation [gate | up] (bf16 [M, 2K], as
+// the wi forward kept it) without rounding dh:
+//   d_gate = dh * up * silu'(gate),  d_up = dh * silu(gate),
+//   silu'(z) = sigma(z) * (1 + z * (1 - sigma(z))),  sigma(z) = 1 / (1 + e^-z).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -86,12 +94,24 @@ __device__ __forceinline__ v4i deq8(uint32_t w0, uint32_t w1, const float* sc) {
                (int)pack_bf16x2(c[0] * sc[4], c[1] * sc[5]), (int)pack_bf16x2(d[0] * sc[6], d[1] * sc[7])};
 }
 
-template <bool FROM_CODES, int BN>
+__device__ __forceinline__ float bf16_lo(int v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
+__device__ __forceinline__ float bf16_hi(int v) { return __builtin_bit_cast(float, (uint32_t)v & 0xffff0000u); }
+
+// gradients of silu(g) * u from the gradient dh of the product (f32)
+__device__ __forceinline__ void dswiglu1(float dh, float g, float u, float& dg, float& du) {
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+  const float t = fmaf(g, 1.0f - sig, 1.0f);
+  dg = dh * u * (sig * t);
+  du = dh * (g * sig);
+}
+
+template <bool FROM_CODES, int BN, bool DSWIGLU>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restrict__ codes,
                      const float* __restrict__ wscale, const uint16_t* __restrict__ wbf16,
                      const int* __restrict__ group_sizes, int G, int M, int K, int N,
-                     uint16_t* __restrict__ dlhs, int* status) {
+                     const uint16_t* __restrict__ preact, uint16_t* __restrict__ dlhs, int* status) {
+  static_assert(!DSWIGLU || FROM_CODES, "the dSwiGLU epilogue belongs to the FP8-code path");
   using C = Cfg<FROM_CODES, BN>;
   constexpr int NJ = C::NJ;
   constexpr int S = C::kStages;
@@ -283,6 +303,39 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   step(ks, F_{}, F_{}, slot(ks + 2), slot(ks), slot(ks + 1));
 
   // ---- epilogue: lane owns row wm*128 + f*16 + lane%16, columns wn*BN/4 + j*16 + 4*(lane/16) + 0..3
+  if (DSWIGLU) {
+    // output and pre-activation rows are [gate | up], 2K wide
+    const size_t ld = 2 * (size_t)K;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int ml = wm * 128 + f * 16 + (lane & 15);
+      if (ml < rows) {
+        const size_t rb = (size_t)(row0 + ml) * ld + nt * BN + wn * (16 * NJ) + 4 * q;
+        v2i gb[NJ], ub[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          gb[j] = *reinterpret_cast<const v2i*>(preact + rb + j * 16);
+          ub[j] = *reinterpret_cast<const v2i*>(preact + rb + K + j * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          float dg[4], du[4];
+          dswiglu1(acc[f][j][0], bf16_lo(gb[j][0]), bf16_lo(ub[j][0]), dg[0], du[0]);
+          dswiglu1(acc[f][j][1], bf16_hi(gb[j][0]), bf16_hi(ub[j][0]), dg[1], du[1]);
+          dswiglu1(acc[f][j][2], bf16_lo(gb[j][1]), bf16_lo(ub[j][1]), dg[2], du[2]);
+          dswiglu1(acc[f][j][3], bf16_hi(gb[j][1]), bf16_hi(ub[j][1]), dg[3], du[3]);
+          v2i pg, pu;
+          pg[0] = (int)pack_bf16x2(dg[0], dg[1]);
+          pg[1] = (int)pack_bf16x2(dg[2], dg[3]);
+          pu[0] = (int)pack_bf16x2(du[0], du[1]);
+          pu[1] = (int)pack_bf16x2(du[2], du[3]);
+          *reinterpret_cast<v2i*>(dlhs + rb + j * 16) = pg;
+          *reinterpret_cast<v2i*>(dlhs + rb + K + j * 16) = pu;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int ml = wm * 128 + f * 16 + (lane & 15);
@@ -299,21 +352,21 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   }
 }
 
-template <bool FROM_CODES>
+template <bool FROM_CODES, bool DSWIGLU>
 hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const float* scale, const uint16_t* wbf16,
-                            const int* group_sizes, int G, int M, int K, int N, uint16_t* dlhs, int* status,
-                            hipStream_t stream) {
+                            const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact,
+                            uint16_t* dlhs, int* status, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const long long max_m_tiles = (M + BM - 1) / BM + G;
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
   if (FROM_CODES && K % 256 == 0) {
-    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 256>), dim3((unsigned)(max_m_tiles * (K / 256))), dim3(kThreads),
-                       (Cfg<FROM_CODES, 256>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K,
-                       N, dlhs, status);
+    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 256, DSWIGLU>), dim3((unsigned)(max_m_tiles * (K / 256))),
+                       dim3(kThreads), (Cfg<FROM_CODES, 256>::kLds + table), stream, dout, codes, scale, wbf16,
+                       group_sizes, G, M, K, N, preact, dlhs, status);
   } else {
-    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 128>), dim3((unsigned)(max_m_tiles * (K / 128))), dim3(kThreads),
-                       (Cfg<FROM_CODES, 128>::kLds + table), stream, dout, codes, scale, wbf16, group_sizes, G, M, K,
-                       N, dlhs, status);
+    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 128, DSWIGLU>), dim3((unsigned)(max_m_tiles * (K / 128))),
+                       dim3(kThreads), (Cfg<FROM_CODES, 128>::kLds + table), stream, dout, codes, scale, wbf16,
+                       group_sizes, G, M, K, N, preact, dlhs, status);
   }
   return hipGetLastError();
 }
@@ -322,12 +375,21 @@ hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const fl
 
 hipError_t launch_gmm_dlhs_fp8(const uint16_t* dout, const uint8_t* codes, const float* scale, const int* group_sizes,
                                int G, int M, int K, int N, uint16_t* dlhs, int* status, hipStream_t stream) {
-  return launch_dlhs_impl<true>(dout, codes, scale, nullptr, group_sizes, G, M, K, N, dlhs, status, stream);
+  return launch_dlhs_impl<true, false>(dout, codes, scale, nullptr, group_sizes, G, M, K, N, nullptr, dlhs, status,
+                                       stream);
+}
+
+hipError_t launch_gmm_dswiglu_fp8(const uint16_t* dout, const uint8_t* codes, const float* scale,
+                                  const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact,
+                                  uint16_t* d_preact, int* status, hipStream_t stream) {
+  return launch_dlhs_impl<true, true>(dout, codes, scale, nullptr, group_sizes, G, M, K, N, preact, d_preact, status,
+                                      stream);
 }
 
 hipError_t launch_gmm_bf16_dlhs(const uint16_t* dout, const uint16_t* w, const int* group_sizes, int G, int M, int K,
                                 int N, uint16_t* dlhs, int* status, hipStream_t stream) {
-  return launch_dlhs_impl<false>(dout, nullptr, nullptr, w, group_sizes, G, M, K, N, dlhs, status, stream);
+  return launch_dlhs_impl<false, false>(dout, nullptr, nullptr, w, group_sizes, G, M, K, N, nullptr, dlhs, status,
+                                        stream);
 }
 
 }  // namespace fp8gmm

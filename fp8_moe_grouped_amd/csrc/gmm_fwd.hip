@@ -5,7 +5,9 @@
 //
 // out[r, n] = bf16( (sum_k dec(aq[r,k]) * dec(codes[g,k,n])) * ascale[r] * wscale[g,n] )
 // for every valid row r of expert g; with SwiGLU the columns are [gate | up]
-// and out[r, i] = bf16( silu(y[r, i]) * y[r, I + i] ), I = N/2.
+// and out[r, i] = bf16( silu(y[r, i]) * y[r, I + i] ), I = N/2, and, when the
+// caller asks for it, the pre-activation preact[r, n] = bf16(y[r, n]) (the
+// values gmm_fp8_fwd would return) is kept for the fused dSwiGLU backward.
 //
 // Tiling (gfx950): a block owns a 256-row x BN-column output tile of one
 // expert, BN = 256 (or 128 when N is not a multiple of 256; for SwiGLU 128
@@ -66,7 +68,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict__ ascale,
                         const uint8_t* __restrict__ codes, const float* __restrict__ wscale,
                         const int* __restrict__ group_sizes, int G, int M, int K, int N,
-                        uint16_t* __restrict__ out, int* status) {
+                        uint16_t* __restrict__ out, uint16_t* __restrict__ preact, int* status) {
   constexpr int NJ = BN / 64;                       // 32-column fragments per wave (BN/2 columns)
   constexpr int MI = 2;                             // 32-row fragments per wave (64 rows)
   constexpr int kStageBytes = stage_bytes<BN>();
@@ -261,17 +263,26 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
             const int c = nt * (BN / 2) + wn * 64 + 32 * j + 8 * q + hl;
             const v4f sg = *reinterpret_cast<const v4f*>(ws + c);
             const v4f su = *reinterpret_cast<const v4f*>(ws + I + c);
-            float o[4];
+            float o[4], yg[4], yu[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float yg = (acc[i][j][4 * q + e] * sr) * sg[e];
-              const float yu = (acc[i][j + 2][4 * q + e] * sr) * su[e];
-              o[e] = yg / (1.0f + __expf(-yg)) * yu;
+              yg[e] = (acc[i][j][4 * q + e] * sr) * sg[e];
+              yu[e] = (acc[i][j + 2][4 * q + e] * sr) * su[e];
+              o[e] = yg[e] / (1.0f + __expf(-yg[e])) * yu[e];
             }
             v2i pk;
             pk[0] = (int)pack_bf16x2(o[0], o[1]);
             pk[1] = (int)pack_bf16x2(o[2], o[3]);
             *reinterpret_cast<v2i*>(out + (size_t)row * I + c) = pk;
+            if (preact) {
+              v2i pg, pu;
+              pg[0] = (int)pack_bf16x2(yg[0], yg[1]);
+              pg[1] = (int)pack_bf16x2(yg[2], yg[3]);
+              pu[0] = (int)pack_bf16x2(yu[0], yu[1]);
+              pu[1] = (int)pack_bf16x2(yu[2], yu[3]);
+              *reinterpret_cast<v2i*>(preact + (size_t)row * N + c) = pg;
+              *reinterpret_cast<v2i*>(preact + (size_t)row * N + I + c) = pu;
+            }
           }
       } else {
 #pragma unroll
@@ -294,7 +305,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 
 hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* wscale,
                               const int* group_sizes, int G, int M, int K, int N, bool swiglu, uint16_t* out,
-                              int* status, hipStream_t stream) {
+                              uint16_t* preact, int* status, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const long long max_m_tiles = (M + BM - 1) / BM + G;
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
@@ -302,17 +313,17 @@ hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint
     const long long grid = max_m_tiles * ((N / 2) / 128);
     hipLaunchKernelGGL((gmm_fp8_fwd_kernel<true, 256>), dim3((unsigned)grid), dim3(kThreads),
                        (lds_main<256>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
-                       status);
+                       swiglu ? preact : nullptr, status);
   } else if (N % 256 == 0) {
     const long long grid = max_m_tiles * (N / 256);
     hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 256>), dim3((unsigned)grid), dim3(kThreads),
                        (lds_main<256>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
-                       status);
+                       swiglu ? preact : nullptr, status);
   } else {
     const long long grid = max_m_tiles * (N / 128);
     hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 128>), dim3((unsigned)grid), dim3(kThreads),
                        (lds_main<128>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
-                       status);
+                       swiglu ? preact : nullptr, status);
   }
   return hipGetLastError();
 }

@@ -38,10 +38,15 @@ hipError_t launch_quant_rows_e4m3(const uint16_t* lhs, const int* group_sizes, i
 
 hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* wscale,
                               const int* group_sizes, int G, int M, int K, int N, bool swiglu, uint16_t* out,
-                              int* status, hipStream_t stream);
+                              uint16_t* preact, int* status, hipStream_t stream);
 
 hipError_t launch_gmm_dlhs_fp8(const uint16_t* dout, const uint8_t* codes, const float* scale, const int* group_sizes,
                                int G, int M, int K, int N, uint16_t* dlhs, int* status, hipStream_t stream);
+
+// dLHS with the dSwiGLU epilogue: preact and d_preact are bf16 [M, 2K].
+hipError_t launch_gmm_dswiglu_fp8(const uint16_t* dout, const uint8_t* codes, const float* scale,
+                                  const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact,
+                                  uint16_t* d_preact, int* status, hipStream_t stream);
 
 hipError_t launch_gmm_bf16_dlhs(const uint16_t* dout, const uint16_t* w, const int* group_sizes, int G, int M, int K,
                                 int N, uint16_t* dlhs, int* status, hipStream_t stream);

@@ -66,6 +66,8 @@ extern "C" {
 #define FP8GMM_OP_TGMM 3
 #define FP8GMM_OP_BF16_FWD 4
 #define FP8GMM_OP_BF16_DLHS 5
+#define FP8GMM_OP_FFN_FWD 6   /* moe_ffn_fp8_fwd: pass K = H, N = I */
+#define FP8GMM_OP_FFN_BWD 7   /* moe_ffn_fp8_bwd: pass K = H, N = I, tile_m = 512 */
 
 /*
  * gmm_fp8_fwd -- native FP8 forward GMM ([P1] Description: the forward GMMs
@@ -95,11 +97,14 @@ int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const
  * Implementation: gmm_silu_fp8).  The N = 2*I weight columns are [gate | up];
  * with y the scaled f32 GEMM result of gmm_fp8_fwd (before rounding):
  *   out[r,i] = bf16( silu(y[r,i]) * y[r,I+i] ),  silu(z) = z / (1 + exp(-z))
- * out is bf16 [M, I].  I must be a multiple of 128.  Other arguments as above.
+ * out is bf16 [M, I].  I must be a multiple of 128.
+ * preact bf16 [M, N] or NULL: receives the pre-activation bf16(y) (exactly
+ *   what gmm_fp8_fwd returns for the same inputs), the residual the fused
+ *   dSwiGLU backward (gmm_dswiglu_fp8) reads.  Other arguments as above.
  */
 int gmm_silu_fp8(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
-                 int64_t M, int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale,
-                 void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+                 int64_t M, int64_t K, int64_t N, int32_t G, void* out, void* preact, uint8_t* dbg_codes,
+                 float* dbg_scale, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
 /*
  * The forward in two calls, for callers whose activations are already e4m3
@@ -121,7 +126,7 @@ int gmm_fp8_fwd_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, 
                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
                   int32_t* dev_status, void* stream);
 int gmm_silu_fp8_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
-                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out,
+                   const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out, void* preact,
                    int32_t* dev_status, void* stream);
 
 /*
@@ -137,6 +142,25 @@ int gmm_silu_fp8_q(const uint8_t* aq, const float* ascale, const uint8_t* codes,
 int gmm_dlhs_fp8(const void* dout, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
                  int64_t M, int64_t K, int64_t N, int32_t G, void* dlhs, void* ws, size_t ws_bytes,
                  int32_t* dev_status, void* stream);
+
+/*
+ * gmm_dswiglu_fp8 -- backward dLHS of the wo GMM fused with the SwiGLU
+ * derivative ([P1] Implementation: gmm_dswiglu_fp8 is the wo op,
+ * _run_wo_gmm_dswiglu; its forward is gmm_fp8_fwd).  With the wo weight
+ * codes [G, K, N] (K = I, the SwiGLU width; N = H, the model width), the wo
+ * output gradient dout bf16 [M, N] and the wi pre-activation preact bf16
+ * [M, 2K] = [gate | up] kept by gmm_silu_fp8:
+ *   dh[r,k]          = sum_n dout[r,n] * w[g,k,n]     f32, not rounded (w as in gmm_dlhs_fp8)
+ *   sigma            = 1 / (1 + exp(-gate[r,k]))
+ *   d_preact[r,k]    = bf16( dh * up[r,k] * sigma * (1 + gate * (1 - sigma)) )
+ *   d_preact[r,K+k]  = bf16( dh * gate * sigma )
+ * d_preact bf16 [M, 2K] is the gradient of the wi pre-activation (rows >=
+ * sum(group_sizes) not written); it feeds gmm_dlhs_fp8 with the wi codes and
+ * tgmm_quant for the wi weight gradient.  Other arguments as gmm_dlhs_fp8.
+ */
+int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                    const void* preact, int64_t M, int64_t K, int64_t N, int32_t G, void* d_preact,
+                    int32_t* dev_status, void* stream);
 
 /*
  * tgmm_quant -- weight gradient with in-kernel operand quantization ([P3]
@@ -180,6 +204,37 @@ int gmm_bf16_fwd(const void* lhs, const void* w, const int32_t* group_sizes, int
                  int32_t G, void* out, int32_t* dev_status, void* stream);
 int gmm_bf16_dlhs(const void* dout, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
                   int32_t G, void* dlhs, int32_t* dev_status, void* stream);
+
+/*
+ * One routed-expert FFN on a static ragged buffer, forward and backward, as
+ * the calls above chain them ([P1] Implementation: gmm_up_or_silu runs
+ * gmm_silu_fp8 for wi and _run_wo_gmm_dswiglu runs gmm_dswiglu_fp8 for wo;
+ * [P3] What: both weight gradients are tgmm_quant).  x bf16 [M, H];
+ * wi codes [G, H, 2I] with scale [G, 2I]; wo codes [G, I, H] with scale
+ * [G, H].  H and I must be multiples of 256 and at most 16384.
+ *
+ * moe_ffn_fp8_fwd: h = gmm_silu_fp8(x, wi) bf16 [M, I] with preact bf16
+ *   [M, 2I] (may be NULL when no backward follows), then
+ *   y = gmm_fp8_fwd(h, wo) bf16 [M, H].  ws: fp8gmm_workspace_bytes(
+ *   FP8GMM_OP_FFN_FWD, M, H, I, G, 0) bytes.
+ * moe_ffn_fp8_bwd: from the forward's x, h, preact and the output gradient
+ *   dy bf16 [M, H]:
+ *     d_preact = gmm_dswiglu_fp8(dy, wo, preact)          bf16 [M, 2I]
+ *     dx       = gmm_dlhs_fp8(d_preact, wi)               bf16 [M, H]  (dx may be NULL: skipped)
+ *     dwo      = tgmm_quant(h, dy, grad_dtype)            f32 [G, I, H]
+ *     dwi      = tgmm_quant(x, d_preact, grad_dtype)      f32 [G, H, 2I]
+ *   tile_m is 512.  ws: fp8gmm_workspace_bytes(FP8GMM_OP_FFN_BWD, M, H, I, G, 512).
+ * Both enqueue their kernels in that order on `stream`; results are those of
+ * the individual calls, bit for bit.
+ */
+int moe_ffn_fp8_fwd(const void* x, const uint8_t* wi_codes, const float* wi_scale, const uint8_t* wo_codes,
+                    const float* wo_scale, const int32_t* group_sizes, int64_t M, int64_t H, int64_t I, int32_t G,
+                    void* h, void* preact, void* y, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+int moe_ffn_fp8_bwd(const void* x, const void* h, const void* preact, const void* dy, const uint8_t* wi_codes,
+                    const float* wi_scale, const uint8_t* wo_codes, const float* wo_scale,
+                    const int32_t* group_sizes, int64_t M, int64_t H, int64_t I, int32_t G, int32_t grad_dtype,
+                    void* d_preact, void* dx, float* dwi, float* dwo, void* ws, size_t ws_bytes,
+                    int32_t* dev_status, void* stream);
 
 /*
  * fp8gmm_workspace_bytes -- device workspace the call `op` needs for these

@@ -92,3 +92,34 @@ def check_f32(gpu, ref_f64, absum, groups_axis0, rows_per_group, what):
     ratio = np.abs(gpu - ref_f64) / tol
     assert ratio.max() <= 1.0, f"{what}: elementwise bound exceeded ({ratio.max():.3f})"
     return tot, max(per)
+
+
+#: largest |silu'(z)| and |silu''(z)| over the reals (about 1.0998 and 0.5)
+SILU1_MAX = 1.0999
+SILU2_MAX = 0.5
+
+
+def dswiglu_tol(res, preact_f64, c_acc, d_preact=None):
+    """Extra elementwise tolerance of the fused dSwiGLU output [d_gate | d_up]:
+    first-order propagation of the f32 accumulation error of dh (c_acc * A +
+    2^-21 |dh|), the f32 evaluation of sigma / silu' (exp, reciprocal, fma),
+    and, with ``d_preact`` (a bound on how far the pre-activation the kernel
+    read may be from the oracle's), the change of the derivative over that
+    distance (|silu''| <= 1/2, |silu'| <= 1.1)."""
+    I = res.dh.shape[1]
+    g, u = preact_f64[:, :I], preact_f64[:, I:]
+    dh = res.dh
+    e_dh = c_acc * res.dh_absum + 2.0 ** -21 * np.abs(dh)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    s1 = sig * (1.0 + g * (1.0 - sig))
+    e_sig = 2.0 ** -22 * (4.0 + np.abs(g))
+    e_s1 = 2.0 ** -20 * (4.0 + np.abs(g))
+    tg = np.abs(u * s1) * e_dh + np.abs(dh * u) * e_s1 + 2.0 ** -20 * np.abs(res.y[:, :I])
+    tu = np.abs(g * sig) * e_dh + np.abs(dh * g) * e_sig + 2.0 ** -20 * np.abs(res.y[:, I:])
+    if d_preact is not None:
+        dg_, du_ = d_preact[:, :I], d_preact[:, I:]
+        a = np.abs(dh) + e_dh
+        tg = tg + a * ((np.abs(u) + du_) * SILU2_MAX * dg_ + SILU1_MAX * du_)
+        tu = tu + a * SILU1_MAX * dg_
+    return np.concatenate([tg, tu], axis=1)

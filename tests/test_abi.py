@@ -36,14 +36,17 @@ def test_header_macros_match_binding():
     assert vals["FP8GMM_ERR_NULL"] == G.ERR_NULL and vals["FP8GMM_ERR_HIP"] == G.ERR_HIP
     assert vals["FP8GMM_E4M3"] == G.E4M3 and vals["FP8GMM_E5M2"] == G.E5M2
     assert vals["FP8GMM_OP_TGMM"] == G.OP_TGMM and vals["FP8GMM_DEV_NEGATIVE_SIZE"] == G.DEV_NEGATIVE_SIZE
+    assert vals["FP8GMM_OP_FFN_FWD"] == G.OP_FFN_FWD and vals["FP8GMM_OP_FFN_BWD"] == G.OP_FFN_BWD
 
 
 P = 0x10000          # fake, 16-byte aligned "device" address; never dereferenced
 BAD = 0x10008        # misaligned
 
 
-def _fwd(L, lhs=P, codes=P, scale=P, gs=P, M=256, K=128, N=256, Gn=4, out=P, ws=P, wsb=1 << 30, fn="gmm_fp8_fwd"):
-    return getattr(L, fn)(lhs, codes, scale, gs, M, K, N, Gn, out, None, None, ws, wsb, None, None)
+def _fwd(L, lhs=P, codes=P, scale=P, gs=P, M=256, K=128, N=256, Gn=4, out=P, ws=P, wsb=1 << 30, fn="gmm_fp8_fwd",
+         preact=None):
+    extra = (preact,) if fn == "gmm_silu_fp8" else ()
+    return getattr(L, fn)(lhs, codes, scale, gs, M, K, N, Gn, out, *extra, None, None, ws, wsb, None, None)
 
 
 def test_forward_validation():
@@ -66,6 +69,43 @@ def test_forward_validation():
         assert _fwd(L, wsb=need - 1, fn=fn) == G.ERR_WORKSPACE
         assert _fwd(L, M=0, ws=None, wsb=0, fn=fn) == G.OK          # empty buffer: a no-op
     assert _fwd(L, N=384, fn="gmm_silu_fp8") == G.ERR_UNSUPPORTED   # I = 192 is not a multiple of 128
+    assert _fwd(L, preact=BAD, fn="gmm_silu_fp8") == G.ERR_ALIGN
+
+
+def test_dswiglu_and_ffn_validation():
+    L = _lib()
+    dsw = lambda **kw: L.gmm_dswiglu_fp8(kw.get("dout", P), P, P, P, kw.get("pre", P), kw.get("M", 64),
+                                         kw.get("K", 256), 512, 2, kw.get("out", P), None, None)
+    assert dsw(pre=None) == G.ERR_NULL
+    assert dsw(out=None) == G.ERR_NULL
+    assert dsw(M=0, pre=None, out=None, dout=None) == G.OK
+    assert dsw(K=192) == G.ERR_UNSUPPORTED
+    assert dsw(pre=BAD) == G.ERR_ALIGN
+    assert dsw(M=-1) == G.ERR_SHAPE
+    fwd = lambda **kw: L.moe_ffn_fp8_fwd(kw.get("x", P), P, P, P, P, P, kw.get("M", 64), kw.get("H", 512),
+                                         kw.get("I", 256), 2, P, kw.get("pre", P), P, kw.get("ws", P),
+                                         kw.get("wsb", 1 << 30), None, None)
+    assert fwd(x=None) == G.ERR_NULL
+    assert fwd(H=384) == G.ERR_UNSUPPORTED               # tgmm needs multiples of 256
+    assert fwd(I=128) == G.ERR_UNSUPPORTED
+    assert fwd(pre=BAD) == G.ERR_ALIGN
+    assert fwd(ws=None) == G.ERR_WORKSPACE
+    need = L.fp8gmm_workspace_bytes(G.OP_FFN_FWD, 64, 512, 256, 2, 0)
+    assert need >= 64 * 512 + 64 * 4
+    assert fwd(wsb=need - 1) == G.ERR_WORKSPACE
+    assert fwd(M=0, x=None, ws=None, wsb=0) == G.OK
+    bwd = lambda **kw: L.moe_ffn_fp8_bwd(P, P, kw.get("pre", P), P, P, P, P, P, P, kw.get("M", 64), 512, 256, 2,
+                                         kw.get("gd", G.E5M2), P, kw.get("dx", P), kw.get("dwi", P), P,
+                                         kw.get("ws", P), kw.get("wsb", 1 << 30), None, None)
+    assert bwd(pre=None) == G.ERR_NULL
+    assert bwd(dwi=None) == G.ERR_NULL
+    assert bwd(gd=3) == G.ERR_UNSUPPORTED
+    assert bwd(dx=BAD) == G.ERR_ALIGN
+    assert bwd(ws=None) == G.ERR_WORKSPACE
+    need = L.fp8gmm_workspace_bytes(G.OP_FFN_BWD, 64, 512, 256, 2, 512)
+    assert need >= L.fp8gmm_workspace_bytes(G.OP_TGMM, 64, 512, 512, 2, 512)
+    assert bwd(wsb=need - 1) == G.ERR_WORKSPACE
+    assert L.fp8gmm_workspace_bytes(G.OP_FFN_BWD, 64, 512, 256, 2, 256) == 0
 
 
 def test_dlhs_and_tgmm_validation():

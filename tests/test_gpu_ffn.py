@@ -1,0 +1,258 @@
+"""GPU parity of the fused wo dLHS + dSwiGLU (gmm_dswiglu_fp8), of the
+pre-activation kept by gmm_silu_fp8, and of one routed-expert FFN forward +
+backward (moe_ffn_fp8_fwd / moe_ffn_fp8_bwd) against the CPU oracle, through
+the C ABI.
+
+The FFN chain is compared stage by stage with the oracle's own chain on the
+same seeded inputs.  The wi forward, the fused dSwiGLU and the wi dLHS get
+elementwise bounds in which the distance between the GPU's and the oracle's
+upstream values is propagated to first order.  The wo forward and the two
+tgmm weight gradients requantize an upstream bf16 result (h, d_preact) to
+e4m3 / the gradient format: a one-ulp upstream difference can move a code by
+one step there, so those outputs are compared normwise (each op on its own is
+held elementwise by the per-op parity tests).  The FFN entry points must also
+equal the individual calls bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as F
+from oracle import gmm as O
+from tests.parity import C_ACC_FP8, bf16_np, check_bf16, dswiglu_tol, swiglu_tol
+
+pytestmark = pytest.mark.gpu
+SENTINEL = 0x7FA1
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def sentinel(rows, cols):
+    return torch.full((rows, cols), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def bits(t):
+    return t.view(torch.int16)
+
+
+# ---------------------------------------------------------------- gmm_dswiglu_fp8
+
+def run_dswiglu(d, gs=None):
+    import fp8_moe_grouped_amd as G
+    gs = d["group_sizes"] if gs is None else gs
+    M, K = d["M"], d["K"]
+    out = sentinel(M, 2 * K)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    G.gmm_dswiglu_fp8(dev(d["dout"]), dev(d["codes"]), dev(d["scale"]), dev(np.asarray(gs, np.int32)),
+                      dev(d["preact"]), out=out, dev_status=status)
+    torch.cuda.synchronize()
+    return bf16_np(out), int(status.item())
+
+
+def check_dswiglu(d, rows=None):
+    got, st = run_dswiglu(d)
+    res = O.gmm_dswiglu(d["dout"], d["codes"], d["scale"], d["group_sizes"], d["preact"], rows=rows)
+    pre = F.bf16_to_f64(d["preact"][res.rows])
+    c_acc = d["N"] * 2.0 ** -24
+    err = check_bf16(got[res.rows], res.y, np.zeros_like(res.y), res.group, 0.0, "dswiglu",
+                     extra_tol=dswiglu_tol(res, pre, c_acc))
+    assert np.all(got[d["valid"]:] == SENTINEL), "rows past the valid prefix were written"
+    assert st == 0
+    return err
+
+
+@pytest.mark.parametrize("key", ["small", "small128"])
+def test_dswiglu_small(key):
+    """Ragged experts (one empty), a stale garbage tail, both column tilings
+    (K = 256 and K = 128)."""
+    err = check_dswiglu(W.dswiglu(key))
+    print(f"dswiglu {key}: normwise {err[0]:.2e}, ratio {err[1]:.3f}")
+
+
+def test_dswiglu_config2():
+    err = check_dswiglu(W.dswiglu(2))
+    print(f"dswiglu config2: normwise {err[0]:.2e}, ratio {err[1]:.3f}")
+
+
+def test_dswiglu_config3_sampled_rows():
+    """The dropless DeepSeek-V3-like shape (wo K = 2048, N = 7168, 19,661 of
+    32,768 rows valid): every row is computed on the GPU; the oracle checks
+    the first and last rows of every non-empty expert and a seeded sample."""
+    d = W.dswiglu(3)
+    lay = O.layout(d["group_sizes"], d["M"])
+    edge = [r for g in range(d["G"]) if lay.end[g] > lay.start[g] for r in (lay.start[g], lay.end[g] - 1)]
+    rows = np.unique(np.concatenate([edge, np.random.default_rng(3).choice(lay.valid, 96, replace=False)]))
+    err = check_dswiglu(d, rows=rows)
+    print(f"dswiglu config3 ({len(rows)} rows): normwise {err[0]:.2e}, ratio {err[1]:.3f}")
+
+
+def test_dswiglu_carries_the_dlhs_bits():
+    """With gate = 30 (sigma = 1 in f32, so silu'(gate) = 1 and silu(gate) =
+    gate) and up = 1, d_gate = dh exactly: its bits must be gmm_dlhs_fp8's,
+    and d_up = bf16(30 dh)."""
+    import fp8_moe_grouped_amd as G
+    d = W.dswiglu("small")
+    M, K = d["M"], d["K"]
+    pre = np.empty((M, 2 * K), np.uint16)
+    pre[:, :K] = 0x41F0            # 30.0
+    pre[:, K:] = 0x3F80            # 1.0
+    d = dict(d, preact=pre)
+    got, _ = run_dswiglu(d)
+    dl = G.gmm_dlhs_fp8(dev(d["dout"]), dev(d["codes"]), dev(d["scale"]), dev(d["group_sizes"]))
+    torch.cuda.synchronize()
+    mv = d["valid"]
+    ref = bf16_np(dl)[:mv]
+    assert np.array_equal(got[:mv, :K], ref)
+    dh = F.bf16_to_f64(ref)
+    # d_up = bf16(30 dh_f32); bf16(dh) is within half an ulp of dh_f32, so
+    # |d_up - 30 bf16(dh)| <= 30 ulp(dh) / 2 + ulp(30 dh) / 2 <= 1.5 ulp(30 dh)
+    dup = F.bf16_to_f64(got[:mv, K:])
+    assert np.all(np.abs(dup - 30 * dh) <= 1.5 * F.ulp_bf16(np.abs(30 * dh)) + 1e-30)
+
+
+def test_dswiglu_empty_and_all_in_one_expert():
+    d = W.dswiglu("small")
+    got, st = run_dswiglu(d, gs=np.zeros(d["G"], np.int32))
+    assert np.all(got == SENTINEL) and st == 0
+    gs = np.array([0, 0, d["valid"], 0], np.int32)
+    d1 = dict(d, group_sizes=gs)
+    err = check_dswiglu(d1)
+    print(f"dswiglu one expert: normwise {err[0]:.2e}")
+
+
+# ---------------------------------------------------------------- pre-activation of gmm_silu_fp8
+
+@pytest.mark.parametrize("config", [1, 3])
+def test_silu_preact_is_plain_forward(config):
+    """The pre-activation kept by gmm_silu_fp8 is gmm_fp8_fwd's result bit for
+    bit, and keeping it leaves h unchanged."""
+    import fp8_moe_grouped_amd as G
+    d = W.make(config, "wi")
+    lhs, codes, scale, gs = dev(d["lhs"]), dev(d["codes"]), dev(d["scale"]), dev(d["group_sizes"])
+    M, N = d["lhs"].shape[0], d["codes"].shape[2]
+    pre = sentinel(M, N)
+    h1, _ = G.gmm_silu_fp8(lhs, codes, scale, gs, preact=pre)
+    h0 = G.gmm_silu_fp8(lhs, codes, scale, gs)
+    y = G.gmm_fp8_fwd(lhs, codes, scale, gs)
+    qc, qs = G.quantize_rows_fp8(lhs, gs)
+    pre_q = sentinel(M, N)
+    h2 = G.gmm_silu_fp8_q(qc, qs, codes, scale, gs, preact=pre_q)
+    torch.cuda.synchronize()
+    mv = int(d["group_sizes"].sum())
+    assert torch.equal(bits(pre[:mv]), bits(y[:mv]))
+    assert torch.equal(bits(pre_q[:mv]), bits(y[:mv]))
+    assert torch.equal(bits(h1[:mv]), bits(h0[:mv])) and torch.equal(bits(h2[:mv]), bits(h0[:mv]))
+    assert torch.all(bits(pre[mv:]) == SENTINEL)
+
+
+# ---------------------------------------------------------------- FFN forward + backward
+
+def run_ffn(d, grad):
+    import fp8_moe_grouped_amd as G
+    M, H, I = d["M"], d["H"], d["I"]
+    t = {k: dev(d[k]) for k in ("x", "wi_codes", "wi_scale", "wo_codes", "wo_scale", "group_sizes", "dy")}
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h, pre, y = sentinel(M, I), sentinel(M, 2 * I), sentinel(M, H)
+    G.moe_ffn_fp8_fwd(t["x"], t["wi_codes"], t["wi_scale"], t["wo_codes"], t["wo_scale"], t["group_sizes"],
+                      h=h, preact=pre, y=y, dev_status=status)
+    dz, dx = sentinel(M, 2 * I), sentinel(M, H)
+    _, dwi, dwo, _ = G.moe_ffn_fp8_bwd(t["x"], h, pre, t["dy"], t["wi_codes"], t["wi_scale"], t["wo_codes"],
+                                       t["wo_scale"], t["group_sizes"], grad, d_preact=dz, dx=dx,
+                                       dev_status=status)
+    torch.cuda.synchronize()
+    return dict(h=h, preact=pre, y=y, d_preact=dz, dx=dx, dwi=dwi, dwo=dwo, status=int(status.item()), t=t)
+
+
+def normwise(got, ref, groups):
+    worst = 0.0
+    for g in np.unique(groups):
+        sel = groups == g
+        den = np.linalg.norm(ref[sel])
+        worst = max(worst, np.linalg.norm(got[sel] - ref[sel]) / den if den > 0 else np.linalg.norm(got[sel]))
+    return worst
+
+
+@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
+def test_ffn_small_against_oracle(grad):
+    d = W.ffn("small")
+    out = run_ffn(d, grad)
+    assert out["status"] == 0
+    res = O.moe_ffn(d["x"], d["wi_codes"], d["wi_scale"], d["wo_codes"], d["wo_scale"], d["group_sizes"], d["dy"],
+                    grad)
+    mv, I, H = d["valid"], d["I"], d["H"]
+    grp = res.fwd_wi.group
+    # 1. wi forward: pre-activation and h (same inputs as the oracle)
+    pre = bf16_np(out["preact"])
+    check_bf16(pre[:mv], res.fwd_wi.y, res.fwd_wi.absum, grp, C_ACC_FP8, "ffn preact")
+    check_bf16(bf16_np(out["h"])[:mv], res.fwd_wi.out_f64, np.zeros((mv, I)), grp, C_ACC_FP8, "ffn h",
+               extra_tol=swiglu_tol(res.fwd_wi, I))
+    tol_pre = F.ulp_bf16(np.abs(res.fwd_wi.y)) + C_ACC_FP8 * res.fwd_wi.absum + 2.0 ** -21 * np.abs(res.fwd_wi.y)
+    # 2. wo forward of h: normwise (h is requantized)
+    y_err = normwise(F.bf16_to_f64(bf16_np(out["y"])[:mv]), F.bf16_to_f64(res.fwd_wo.out), grp)
+    assert y_err <= 2.0 ** -5, y_err
+    # 3. fused dSwiGLU: the oracle's pre-activation may differ by tol_pre
+    pre_or = F.bf16_to_f64(res.preact)
+    c3 = H * 2.0 ** -24
+    tol_dz = dswiglu_tol(res.dsw, pre_or, c3, d_preact=tol_pre)
+    dz = bf16_np(out["d_preact"])
+    check_bf16(dz[:mv], res.dsw.y, np.zeros_like(res.dsw.y), grp, 0.0, "ffn d_preact", extra_tol=tol_dz)
+    # 4. wi dLHS: propagate the d_preact distance through |w|
+    # |dz_gpu - dz_oracle| <= (bound checked above) + the oracle's own rounding
+    e_dz = tol_dz + 2 * F.ulp_bf16(np.abs(res.dsw.y) + tol_dz) + 2.0 ** -21 * np.abs(res.dsw.y)
+    wabs = np.abs(F.bf16_to_f64(O.dequantize(d["wi_codes"], d["wi_scale"])))     # [G, H, 2I]
+    prop = np.stack([e_dz[i] @ wabs[grp[i]].T for i in range(mv)])
+    check_bf16(bf16_np(out["dx"])[:mv], res.dx.y, res.dx.absum, grp, 2 * I * 2.0 ** -24, "ffn dx",
+               extra_tol=prop)
+    # 5. weight gradients: normwise against the oracle chain
+    for name, got, ref in (("dwo", out["dwo"], res.dwo.drhs_f64), ("dwi", out["dwi"], res.dwi.drhs_f64)):
+        g = got.cpu().numpy().astype(np.float64)
+        for e in range(d["G"]):
+            den = np.linalg.norm(ref[e])
+            if den == 0:
+                assert np.all(g[e] == 0), f"{name}: expert {e} must be zero"
+                continue
+            rel = np.linalg.norm(g[e] - ref[e]) / den
+            assert rel <= 2.0 ** -4, f"{name} expert {e}: {rel:.3e}"
+    # stale rows untouched
+    for k in ("h", "preact", "y", "d_preact", "dx"):
+        assert torch.all(bits(out[k][mv:]) == SENTINEL), k
+    print(f"ffn small {grad}: y normwise {y_err:.2e}")
+
+
+@pytest.mark.parametrize("key", ["small", 3])
+def test_ffn_equals_individual_calls(key):
+    """moe_ffn_fp8_fwd / _bwd give the individual calls' results bit for bit
+    (the DeepSeek-V3-like dropless shape at full size)."""
+    import fp8_moe_grouped_amd as G
+    d = W.ffn(key)
+    out = run_ffn(d, "e5m2")
+    t = out["t"]
+    mv = d["valid"]
+    h, pre = G.gmm_silu_fp8(t["x"], t["wi_codes"], t["wi_scale"], t["group_sizes"], preact=True)
+    y = G.gmm_fp8_fwd(out["h"], t["wo_codes"], t["wo_scale"], t["group_sizes"])
+    dz = G.gmm_dswiglu_fp8(t["dy"], t["wo_codes"], t["wo_scale"], t["group_sizes"], out["preact"])
+    dx = G.gmm_dlhs_fp8(out["d_preact"], t["wi_codes"], t["wi_scale"], t["group_sizes"])
+    dwo = G.tgmm_quant(out["h"], t["dy"], t["group_sizes"], "e5m2")
+    dwi = G.tgmm_quant(t["x"], out["d_preact"], t["group_sizes"], "e5m2")
+    torch.cuda.synchronize()
+    for name, a, b in (("h", h, out["h"]), ("preact", pre, out["preact"]), ("y", y, out["y"]),
+                       ("d_preact", dz, out["d_preact"]), ("dx", dx, out["dx"])):
+        assert torch.equal(bits(a[:mv]), bits(b[:mv])), name
+    assert torch.equal(dwo, out["dwo"]) and torch.equal(dwi, out["dwi"])
+    assert torch.isfinite(out["dwi"]).all() and torch.isfinite(out["dwo"]).all()
+
+
+def test_ffn_without_rows():
+    """No valid rows: the row outputs stay untouched, the weight gradients are zeros."""
+    d = W.ffn("small")
+    d = dict(d, group_sizes=np.zeros(d["G"], np.int32))
+    out = run_ffn(d, "e4m3")
+    for k in ("h", "preact", "y", "d_preact", "dx"):
+        assert torch.all(bits(out[k]) == SENTINEL), k
+    assert torch.count_nonzero(out["dwi"]) == 0 and torch.count_nonzero(out["dwo"]) == 0

@@ -23,6 +23,11 @@ Workloads (sizes from the task's five configurations):
 4     tgmm on the config-3 buffer: lhs [32768, 7168], dout [32768, 2048],
       tile_m = 512
 ====  =====================================================================
+
+The fused dSwiGLU backward and the FFN forward/backward reuse these shapes
+(``dswiglu`` and ``ffn`` below): the wi pre-activation [gate | up] is drawn
+N(0, 2^2) in bf16, so every region of silu' (its zero near -1.28, the
+saturated tails) is populated.
 """
 from __future__ import annotations
 
@@ -35,6 +40,7 @@ GARBAGE_BF16 = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFFF, 0x7F7F], dtype=np.uint1
 
 # stream ids, one per tensor role
 ROUTING, LHS_WI, LHS_WO, OUTLIERS_WI, OUTLIERS_WO, W_WI, W_WO, DOUT_WI, DOUT_WO, LHS, DOUT = range(11)
+PREACT, FFN_X, FFN_X_OUT, FFN_WI, FFN_WO, FFN_DY = range(11, 17)
 
 SHAPES = {
     0: dict(G=4, M=256, K=128, N=256),
@@ -204,3 +210,62 @@ def make(config: int, op: str, variant: str | None = None) -> dict:
                     lhs=activations(4, LHS, M, K, valid, outlier_stream=OUTLIERS_WI),
                     dout=gradients(4, DOUT, M, N, valid))
     raise ValueError(config)
+
+
+def preactivations(config: int, M: int, I2: int, valid: int, std: float = 2.0) -> np.ndarray:
+    """bf16 [M, 2I] wi pre-activations ~ N(0, std) on valid rows, garbage after."""
+    r = rng(config, PREACT)
+    z = r.standard_normal((valid, I2), dtype=np.float32) * np.float32(std)
+    out = np.empty((M, I2), dtype=np.uint16)
+    out[:valid] = to_bf16_bits(z)
+    fill_garbage(out, valid)
+    return out
+
+
+#: FFN / dSwiGLU shapes: small (ragged, static tail), config 2's wo, config 3's
+FFN_SHAPES = {
+    "small": dict(G=4, M=320, valid=None, H=256, I=256),
+    "small128": dict(G=4, M=320, valid=None, H=256, I=128),
+    2: dict(G=8, M=8192, valid=8192, H=2048, I=768),
+    3: dict(G=32, M=32768, valid=SHAPES[3]["valid"], H=7168, I=2048),
+}
+
+
+def _ffn_sizes(key):
+    sh = FFN_SHAPES[key]
+    if key in ("small", "small128"):
+        r = rng(90, ROUTING)
+        cuts = np.sort(r.integers(0, 257, size=2))
+        parts = np.diff(np.concatenate([[0], cuts, [256]]))
+        return np.array([parts[0], 0, parts[1], parts[2]], dtype=np.int32)   # one empty expert
+    return group_sizes(key)
+
+
+def dswiglu(key) -> dict:
+    """Inputs of the fused wo dLHS + dSwiGLU: dout [M, H] ~ N(0, 1e-3), wo codes
+    [G, I, H], preact [M, 2I] ~ N(0, 4); stale rows hold garbage."""
+    sh = FFN_SHAPES[key]
+    G, M, H, I = sh["G"], sh["M"], sh["H"], sh["I"]
+    gs = _ffn_sizes(key)
+    valid = int(gs.sum())
+    c = 90 if key in ("small", "small128") else key
+    codes, scale = weights(c, W_WO, G, I, H)
+    return dict(G=G, M=M, K=I, N=H, valid=valid, group_sizes=gs, codes=codes, scale=scale,
+                dout=gradients(c, DOUT_WO, M, H, valid), preact=preactivations(c, M, 2 * I, valid))
+
+
+def ffn(key) -> dict:
+    """Inputs of one routed-expert FFN forward + backward: x [M, H] ~ N(0, 1)
+    with 1% outliers x50, wi [G, H, 2I] and wo [G, I, H] ~ N(0, 0.02) as
+    codes + scales, dy [M, H] ~ N(0, 1e-3); stale rows hold garbage."""
+    sh = FFN_SHAPES[key]
+    G, M, H, I = sh["G"], sh["M"], sh["H"], sh["I"]
+    gs = _ffn_sizes(key)
+    valid = int(gs.sum())
+    c = 91 if key in ("small", "small128") else key
+    wi_codes, wi_scale = weights(c, FFN_WI, G, H, 2 * I)
+    wo_codes, wo_scale = weights(c, FFN_WO, G, I, H)
+    return dict(G=G, M=M, H=H, I=I, valid=valid, group_sizes=gs, wi_codes=wi_codes, wi_scale=wi_scale,
+                wo_codes=wo_codes, wo_scale=wo_scale,
+                x=activations(c, FFN_X, M, H, valid, outlier_stream=FFN_X_OUT),
+                dy=gradients(c, FFN_DY, M, H, valid))
