@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
 # were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "0807c470a7e2a627", 2258, 77),
-    "wo_gemm": ("gmm_fwd.hip", "0807c470a7e2a627", 840, 270),
-    "wi_dlhs": ("dlhs.hip", "7ecd4023bd753326", 2289, 269),
-    "wo_dlhs": ("dlhs.hip", "7ecd4023bd753326", 1262, 77),
-    "tgmm": ("tgmm.hip", "60954c8f6c6016d5", 346 + 1450, 188 + 1929),
-    "dequant": ("dequant.hip", "5576245b9a9d9b08", 455, 976),
+    "wi_gemm": ("gmm_fwd.hip", "f534e57c1835e170", 2272, 77),
+    "wo_gemm": ("gmm_fwd.hip", "f534e57c1835e170", 841, 270),
+    "wi_dlhs": ("dlhs.hip", "1131d62936e0d936", 2292, 269),
+    "wo_dlhs": ("dlhs.hip", "1131d62936e0d936", 1263, 77),
+    "tgmm": ("tgmm.hip", "20bc23075088ca5b", 346 + 1454, 188 + 1928),
+    "dequant": ("dequant.hip", "5ae244463b4e54e8", 455, 979),
 }
 
 
@@ -155,6 +155,78 @@ def cpu_baseline(d, seconds_target):
                       f"spread over the experts; {dt:.1f}s"}
 
 
+def ffn_step(G, args, gs, x, wi_codes, wi_scale, wo_codes, wo_scale, dy, mv, stream):
+    """One routed-expert FFN forward + backward on the same buffer (H = 7168,
+    I = 2048): moe_ffn_fp8_fwd then moe_ffn_fp8_bwd (e5m2 gradients), timed
+    with HIP events on the launch stream; then each backward op alone."""
+    import torch
+    M, H = x.shape
+    I = wo_codes.shape[1]
+    dev = x.device
+    h = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    pre = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dz = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dwi = torch.empty((32, H, 2 * I), dtype=torch.float32, device=dev)
+    dwo = torch.empty((32, I, H), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(G.workspace_bytes(G.OP_FFN_FWD, M, H, I, 32, 0), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(G.workspace_bytes(G.OP_FFN_BWD, M, H, I, 32, 512), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        G.moe_ffn_fp8_fwd(x, wi_codes, wi_scale, wo_codes, wo_scale, gs, h=h, preact=pre, y=y, workspace=ws_f)
+
+    def bwd():
+        G.moe_ffn_fp8_bwd(x, h, pre, dy, wi_codes, wi_scale, wo_codes, wo_scale, gs, "e5m2", d_preact=dz, dx=dx,
+                          dwi=dwi, dwo=dwo, workspace=ws_b)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    ms_f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    # the backward's calls one by one (same kernels, same buffers)
+    parts = [
+        ("dswiglu", 2.0 * mv * I * H, lambda: G.gmm_dswiglu_fp8(dy, wo_codes, wo_scale, gs, pre, out=dz)),
+        ("wi_dlhs", 4.0 * mv * I * H, lambda: G.gmm_dlhs_fp8(dz, wi_codes, wi_scale, gs, out=dx)),
+        ("tgmm_wo", 2.0 * mv * I * H, lambda: G.tgmm_quant(h, dy, gs, "e5m2", 512, out=dwo, workspace=ws_b)),
+        ("tgmm_wi", 4.0 * mv * I * H, lambda: G.tgmm_quant(x, dz, gs, "e5m2", 512, out=dwi, workspace=ws_b)),
+    ]
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+    for e in pev:
+        for i, (_, _, fn) in enumerate(parts):
+            e[i].record(stream)
+            fn()
+        e[-1].record(stream)
+    torch.cuda.synchronize()
+    bwd_ops = {}
+    for i, (name, fl, _) in enumerate(parts):
+        ms = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in pev]))
+        bwd_ops[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    fl_f = 6.0 * mv * H * I
+    fl_b = 12.0 * mv * H * I
+    del dwi, dwo
+    return {
+        "workload": "one MoE FFN forward + backward on the dropless buffer: H=7168, I=2048, G=32, "
+                    f"{mv} valid rows; e5m2 gradients",
+        "ms_fwd": round(ms_f, 4), "ms_bwd": round(ms_b, 4), "ms_step": round(ms_f + ms_b, 4),
+        "tflop_per_step": round((fl_f + fl_b) / 1e12, 4),
+        "tflops": round((fl_f + fl_b) / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
+        "tflops_fwd": round(fl_f / (ms_f * 1e-3) / 1e12, 2),
+        "tflops_bwd": round(fl_b / (ms_b * 1e-3) / 1e12, 2),
+        "bwd_ops": bwd_ops,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +235,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-arm", action="store_true")
+    ap.add_argument("--no-ffn", action="store_true", help="skip the MoE FFN forward + backward measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy (read MIB, write MIB) three times; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE hardware counters to bytes")
@@ -317,6 +390,9 @@ def main():
                  "pages_tpu7x": {"wi": 1.635, "wo": 1.731}}
         del w_wi
 
+    ffn = None if args.no_ffn else ffn_step(G, args, gs, lhs_wi, codes_wi, scale_wi, codes_wo, scale_wo, dout_wo,
+                                            int(np.sum(d["gs"])), stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(d, args.cpu_seconds)
@@ -347,6 +423,7 @@ def main():
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
         "fp8_over_bf16": ({k: (round(v, 3) if isinstance(v, float) else v) for k, v in ratio.items()}
                           if ratio else None),
+        "ffn_step": ffn,
     }
     print(json.dumps(line), flush=True)
 
