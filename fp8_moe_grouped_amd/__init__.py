@@ -57,6 +57,7 @@ _SIGNATURES = {
     "moe_ffn_fp8_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P,
                         _SZ, _P, _P],
     "gmm_bf16_fwd": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
+    "gmm_bf16_silu": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
     "gmm_bf16_dlhs": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
 }
 
@@ -403,8 +404,7 @@ def dequantize_fp8_codes(codes, scale, *, out=None):
     return out
 
 
-def gmm_bf16_fwd(lhs, w, group_sizes, *, out=None, workspace=None):
-    """bf16 x bf16 grouped GEMM (the bf16 measurement arm); bf16 [M, N]."""
+def _bf16_fwd(name, lhs, w, group_sizes, out, swiglu, dev_status):
     _req(lhs, "lhs", torch.bfloat16, 2)
     _req(w, "w", torch.bfloat16, 3)
     _req(group_sizes, "group_sizes", torch.int32, 1)
@@ -414,10 +414,22 @@ def gmm_bf16_fwd(lhs, w, group_sizes, *, out=None, workspace=None):
     if K2 != K or group_sizes.shape[0] != G:
         raise ValueError("shape mismatch")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((M, N // 2 if swiglu else N), dtype=torch.bfloat16, device=dev)
+    _req(out, "out", torch.bfloat16, 2)
     with torch.cuda.device(dev):
-        _call("gmm_bf16_fwd", _ptr(lhs), _ptr(w), _ptr(group_sizes), M, K, N, G, _ptr(out), None, _stream(dev))
+        _call(name, _ptr(lhs), _ptr(w), _ptr(group_sizes), M, K, N, G, _ptr(out), _ptr(dev_status), _stream(dev))
     return out
+
+
+def gmm_bf16_fwd(lhs, w, group_sizes, *, out=None, dev_status=None):
+    """bf16 x bf16 grouped GEMM (the bf16 measurement arm); bf16 [M, N]."""
+    return _bf16_fwd("gmm_bf16_fwd", lhs, w, group_sizes, out, False, dev_status)
+
+
+def gmm_bf16_silu(lhs, w, group_sizes, *, out=None, dev_status=None):
+    """bf16 grouped GEMM with the SwiGLU epilogue over [gate | up] (the bf16
+    arm of gmm_silu_fp8); bf16 [M, N/2]."""
+    return _bf16_fwd("gmm_bf16_silu", lhs, w, group_sizes, out, True, dev_status)
 
 
 def gmm_bf16_dlhs(dout, w, group_sizes, *, out=None):

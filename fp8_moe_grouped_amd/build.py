@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8_moe_grouped.so")
 
-SOURCES = ["quant.hip", "gmm_fwd.hip", "gmm_bf16.hip", "dlhs.hip", "tgmm.hip", "dequant.hip", "api.hip"]
+SOURCES = ["quant.hip", "gmm_fwd.hip", "dlhs.hip", "tgmm.hip", "dequant.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

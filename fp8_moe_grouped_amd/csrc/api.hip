@@ -184,19 +184,31 @@ int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, 
   return FP8GMM_OK;
 }
 
-int gmm_bf16_fwd(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
-                 int32_t G, void* out, int32_t* dev_status, void* stream) {
+static int bf16_fwd_common(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K,
+                           int64_t N, int32_t G, void* out, int32_t* dev_status, void* stream, bool swiglu) {
   if (!w || !group_sizes) return FP8GMM_ERR_NULL;
   int st = check_common(M, K, N, G);
   if (st != FP8GMM_OK) return st;
   if (M > 0 && (!lhs || !out)) return FP8GMM_ERR_NULL;
+  if (swiglu && ((N / 2) % 128 != 0)) return FP8GMM_ERR_UNSUPPORTED;
+  if ((long long)K * N * 2 >= (1LL << 32)) return FP8GMM_ERR_UNSUPPORTED;   // one expert's bf16 weight per range
   if (!aligned16(lhs) || !aligned16(w) || !aligned16(out)) return FP8GMM_ERR_ALIGN;
   if (M == 0) return FP8GMM_OK;
   if (launch_gmm_bf16_fwd(static_cast<const uint16_t*>(lhs), static_cast<const uint16_t*>(w), group_sizes, G, (int)M,
-                          (int)K, (int)N, static_cast<uint16_t*>(out), dev_status,
+                          (int)K, (int)N, swiglu, static_cast<uint16_t*>(out), dev_status,
                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return FP8GMM_ERR_HIP;
   return FP8GMM_OK;
+}
+
+int gmm_bf16_fwd(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                 int32_t G, void* out, int32_t* dev_status, void* stream) {
+  return bf16_fwd_common(lhs, w, group_sizes, M, K, N, G, out, dev_status, stream, false);
+}
+
+int gmm_bf16_silu(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                  int32_t G, void* out, int32_t* dev_status, void* stream) {
+  return bf16_fwd_common(lhs, w, group_sizes, M, K, N, G, out, dev_status, stream, true);
 }
 
 int gmm_bf16_dlhs(const void* dout, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,

@@ -58,12 +58,32 @@ constexpr int lds_main() { return kStages * stage_bytes<BN>(); }
 // one chunk, and two transposing-read groups (8 weight rows each, adjacent
 // chunks), hit distinct banks.
 __device__ __forceinline__ int a_swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4); }
-template <int BN>
-__device__ __forceinline__ int b_key(int k) { return BN == 256 ? ((k & 7) << 1) : (((k >> 1) & 3) << 1); }
-template <int BN>
-__device__ __forceinline__ int b_swz(int k, int chunk) { return k * BN + ((chunk ^ b_key<BN>(k)) << 4); }
+//   FP8 weights: a transposing-read group covers 8 weight rows x 16 bytes;
+//   bf16 weights: 4 weight rows x 32 bytes (rows are 2*BN bytes).
+template <bool BF16, int BN>
+__device__ __forceinline__ int b_key(int k) {
+  return BF16 ? ((k & 3) << 2) : (BN == 256 ? ((k & 7) << 1) : (((k >> 1) & 3) << 1));
+}
+template <bool BF16, int BN>
+__device__ __forceinline__ int b_swz(int k, int chunk) {
+  return k * (BF16 ? 2 * BN : BN) + ((chunk ^ b_key<BF16, BN>(k)) << 4);
+}
 
-template <bool SWIGLU, int BN>
+// Transposing read of four consecutive k (rows) of one bf16 column: within each
+// 16-lane group lane i receives element j from addr[4j + (i>>2)] + 2*(i&3)
+// bytes, addr[L] being lane L's address.
+__device__ __forceinline__ v2i lds_read_tr16(const void* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4s, const_cast<void*>(p)));
+  return __builtin_bit_cast(v2i, v);
+}
+
+// BF16 = false: the FP8 forward (aq / codes are e4m3 bytes, scaled epilogue).
+// BF16 = true: the bf16 measurement arm on the same schedule, ring and wave
+// layout: aq / codes hold bf16 activations / weights, a stage still moves 64
+// bytes of every activation row (32 k) and 32 weight rows of 2*BN bytes, each
+// fragment takes two 32x32x16 bf16 MFMAs, and the epilogue has no scales.
+template <bool BF16, bool SWIGLU, int BN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict__ ascale,
                         const uint8_t* __restrict__ codes, const float* __restrict__ wscale,
@@ -71,12 +91,14 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
                         uint16_t* __restrict__ out, uint16_t* __restrict__ preact, int* status) {
   constexpr int NJ = BN / 64;                       // 32-column fragments per wave (BN/2 columns)
   constexpr int MI = 2;                             // 32-row fragments per wave (64 rows)
+  constexpr int kEl = BF16 ? 2 : 1;                 // bytes per element
   constexpr int kStageBytes = stage_bytes<BN>();
-  constexpr int kBChunks = BN / 16;                 // 16-byte chunks per weight-tile row
+  constexpr int kBRow = BN * kEl;                   // bytes per weight-tile row
+  constexpr int kBChunks = kBRow / 16;              // 16-byte chunks per weight-tile row
   constexpr int kALoads = BM * BK / 1024 / 8;       // 1 KB wave-wide copies per wave per stage
   constexpr int kBLoads = BK * BN / 1024 / 8;
   constexpr int kLoads = kALoads + kBLoads;
-  constexpr int kBRowsPerLoad = 1024 / BN;
+  constexpr int kBRowsPerLoad = 1024 / kBRow;
   static_assert(!SWIGLU || BN == 256, "SwiGLU pairs 2 gate with 2 up fragments per wave");
   static_assert(kLoads * (kStages - 1) < 64, "outstanding copies fit vmcnt");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -110,40 +132,49 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   const int rows = __builtin_amdgcn_readfirstlane(min(BM, t_end[g] - row0));
 
   // ---- buffer resources: the tile's activation rows and the expert's codes
-  const BufRsrc ra = make_rsrc(aq + (size_t)row0 * K, (uint32_t)rows * (uint32_t)K);
-  const BufRsrc rb = make_rsrc(codes + (size_t)g * K * N, (uint32_t)K * (uint32_t)N);
+  const BufRsrc ra = make_rsrc(aq + (size_t)row0 * K * kEl, (uint32_t)rows * (uint32_t)K * kEl);
+  const BufRsrc rb = make_rsrc(codes + (size_t)g * K * N * kEl, (uint32_t)K * (uint32_t)N * kEl);
   uint32_t va[kALoads];                // activation chunk offsets (stage 0)
 #pragma unroll
   for (int j = 0; j < kALoads; ++j) {
     const int r = (kALoads * wave + j) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    va[j] = (uint32_t)min(r, rows - 1) * (uint32_t)K + (uint32_t)(c << 4);
+    va[j] = (uint32_t)min(r, rows - 1) * (uint32_t)K * kEl + (uint32_t)(c << 4);
   }
   uint32_t vb[kBLoads];                // weight chunk offsets (stage 0)
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j) {
+    constexpr int kHalf = kBChunks / 2, kChunkEl = 16 / kEl;
     const int kk = (kBLoads * wave + j) * kBRowsPerLoad + lane / kBChunks;
-    const int c = (lane % kBChunks) ^ b_key<BN>(kk);
+    const int c = (lane % kBChunks) ^ b_key<BF16, BN>(kk);
     int col;
-    if (SWIGLU) col = (c < 8) ? nt * (BN / 2) + (c << 4) : I + nt * (BN / 2) + ((c - 8) << 4);
-    else col = nt * BN + (c << 4);
-    vb[j] = (uint32_t)kk * (uint32_t)N + (uint32_t)col;
+    if (SWIGLU) col = (c < kHalf) ? nt * (BN / 2) + c * kChunkEl : I + nt * (BN / 2) + (c - kHalf) * kChunkEl;
+    else col = nt * BN + c * kChunkEl;
+    vb[j] = ((uint32_t)kk * (uint32_t)N + (uint32_t)col) * kEl;
   }
 
   // ---- per-lane LDS read offsets of the MFMA operands (within a stage)
   int a_rd[2];                         // + i * 32 rows
 #pragma unroll
   for (int h = 0; h < 2; ++h) a_rd[h] = a_swz(wm * 64 + (lane & 31), 2 * (lane >> 5) + h);
-  int b_rd[NJ];                        // + t * 8 rows
+  // Weight operand: lanes 0-31 take k 0..BK/2-1 of the stage (in bytes), lanes
+  // 32-63 the rest; the activation operand uses the same split, so every MFMA
+  // pairs the same k on both sides.
+  int b_rd[NJ];                        // + t * (8 FP8 | 4 bf16) rows
   {
     const int gq = lane >> 4, Lg = lane & 15;
-    const int kk = (gq >> 1) * 32 + (Lg >> 1);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       int tc;                          // first tile column of fragment j
       if (SWIGLU) tc = (j < 2) ? wn * 64 + 32 * j : 128 + wn * 64 + 32 * (j - 2);
       else tc = wn * (BN / 2) + 32 * j;
-      b_rd[j] = BM * BK + b_swz<BN>(kk, (tc >> 4) + (gq & 1)) + 8 * (Lg & 1);
+      if (BF16) {
+        const int kk = (gq >> 1) * 16 + (Lg >> 2);
+        b_rd[j] = BM * BK + b_swz<BF16, BN>(kk, (tc >> 3) + 2 * (gq & 1) + ((Lg & 3) >> 1)) + 8 * (Lg & 1);
+      } else {
+        const int kk = (gq >> 1) * 32 + (Lg >> 1);
+        b_rd[j] = BM * BK + b_swz<BF16, BN>(kk, (tc >> 4) + (gq & 1)) + 8 * (Lg & 1);
+      }
     }
   }
 
@@ -162,11 +193,22 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
     v8i r;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const v2i v = lds_read_tr8(S + t * 8 * BN);
+      const v2i v = BF16 ? lds_read_tr16(S + t * 4 * kBRow) : lds_read_tr8(S + t * 8 * kBRow);
       r[2 * t] = v[0];
       r[2 * t + 1] = v[1];
     }
     return r;
+  };
+  // one stage of fragment (i, j): FP8 one 32x32x64, bf16 two 32x32x16 (the
+  // halves of the lane's 32 bytes)
+  auto mma = [&](const v8i& bw, const v8i& av, const v16f& c) {
+    if (BF16) {
+      const v16f c1 = mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, (v4i){bw[0], bw[1], bw[2], bw[3]}),
+                                         __builtin_bit_cast(v8bf, (v4i){av[0], av[1], av[2], av[3]}), c);
+      return mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, (v4i){bw[4], bw[5], bw[6], bw[7]}),
+                                __builtin_bit_cast(v8bf, (v4i){av[4], av[5], av[6], av[7]}), c1);
+    }
+    return mfma_e4m3_32x32x64(bw, av, c);
   };
 
   v16f acc[MI][NJ];
@@ -177,7 +219,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / BK;
+  const int nk = K * kEl / BK;
 
   // ---- prologue: stages 0..3 in flight, stage 0 landed and in registers
   const int pre = min(nk, kStages);
@@ -223,7 +265,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
         for (int q = j * kLoads / NJ; q < (j + 1) * kLoads / NJ; ++q) issue_one(wr, ks + kStages, q);
       }
 #pragma unroll
-      for (int i = 0; i < MI; ++i) acc[i][j] = mfma_e4m3_32x32x64(bf[j], a[i], acc[i][j]);
+      for (int i = 0; i < MI; ++i) acc[i][j] = mma(bf[j], a[i], acc[i][j]);
       if (MORE) bf[j] = read_b(rd, j);
       sched_fence();   // keep each refill between the MFMAs that surround it
     }
@@ -247,22 +289,24 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 
   // ---- epilogue: lane owns row wm*64 + i*32 + lane%32 and, per fragment j,
   // columns tc(j) + 8*q + 4*(lane/32) + 0..3 for q = 0..3
-  const float* ws = wscale + (size_t)g * N;
+  const float* ws = BF16 ? nullptr : wscale + (size_t)g * N;
+  const v4f ones = {1.f, 1.f, 1.f, 1.f};
   const int hl = 4 * (lane >> 5);
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int ml = wm * 64 + i * 32 + (lane & 31);
     if (ml < rows) {
       const int row = row0 + ml;
-      const float sr = ascale[row];
+      const float sr = BF16 ? 1.f : ascale[row];
       if (SWIGLU) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+          v2i pgq[4], puq[4];   // pre-activation of columns 8q + hl + 0..3, gate and up
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = nt * (BN / 2) + wn * 64 + 32 * j + 8 * q + hl;
-            const v4f sg = *reinterpret_cast<const v4f*>(ws + c);
-            const v4f su = *reinterpret_cast<const v4f*>(ws + I + c);
+            const v4f sg = BF16 ? ones : *reinterpret_cast<const v4f*>(ws + c);
+            const v4f su = BF16 ? ones : *reinterpret_cast<const v4f*>(ws + I + c);
             float o[4], yg[4], yu[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -274,23 +318,40 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
             pk[0] = (int)pack_bf16x2(o[0], o[1]);
             pk[1] = (int)pack_bf16x2(o[2], o[3]);
             *reinterpret_cast<v2i*>(out + (size_t)row * I + c) = pk;
-            if (preact) {
-              v2i pg, pu;
-              pg[0] = (int)pack_bf16x2(yg[0], yg[1]);
-              pg[1] = (int)pack_bf16x2(yg[2], yg[3]);
-              pu[0] = (int)pack_bf16x2(yu[0], yu[1]);
-              pu[1] = (int)pack_bf16x2(yu[2], yu[3]);
-              *reinterpret_cast<v2i*>(preact + (size_t)row * N + c) = pg;
-              *reinterpret_cast<v2i*>(preact + (size_t)row * N + I + c) = pu;
+            pgq[q][0] = (int)pack_bf16x2(yg[0], yg[1]);
+            pgq[q][1] = (int)pack_bf16x2(yg[2], yg[3]);
+            puq[q][0] = (int)pack_bf16x2(yu[0], yu[1]);
+            puq[q][1] = (int)pack_bf16x2(yu[2], yu[3]);
+          }
+          if (preact) {
+            // Lanes l and l+32 hold the same row, columns 8q+0..3 and 8q+4..7.  Trading one
+            // 8-byte half per column pair makes each lane own 8 consecutive columns, so the
+            // pre-activation leaves in 16-byte stores (with 8-byte stores the L2 writes
+            // these lines back about twice).
+            const bool lo = (lane & 32) == 0;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const v2i sg = lo ? pgq[2 * p + 1] : pgq[2 * p];
+              const v2i su = lo ? puq[2 * p + 1] : puq[2 * p];
+              const int rg0 = __shfl_xor(sg[0], 32), rg1 = __shfl_xor(sg[1], 32);
+              const int ru0 = __shfl_xor(su[0], 32), ru1 = __shfl_xor(su[1], 32);
+              const v4i g4 = lo ? (v4i){pgq[2 * p][0], pgq[2 * p][1], rg0, rg1}
+                                : (v4i){rg0, rg1, pgq[2 * p + 1][0], pgq[2 * p + 1][1]};
+              const v4i u4 = lo ? (v4i){puq[2 * p][0], puq[2 * p][1], ru0, ru1}
+                                : (v4i){ru0, ru1, puq[2 * p + 1][0], puq[2 * p + 1][1]};
+              const int cb = nt * (BN / 2) + wn * 64 + 32 * j + 16 * p + (lo ? 0 : 8);
+              *reinterpret_cast<v4i*>(preact + (size_t)row * N + cb) = g4;
+              *reinterpret_cast<v4i*>(preact + (size_t)row * N + I + cb) = u4;
             }
           }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = nt * BN + wn * (BN / 2) + 32 * j + 8 * q + hl;
-            const v4f sc = *reinterpret_cast<const v4f*>(ws + c);
+            const v4f sc = BF16 ? ones : *reinterpret_cast<const v4f*>(ws + c);
             v2i pk;
             pk[0] = (int)pack_bf16x2((acc[i][j][4 * q] * sr) * sc[0], (acc[i][j][4 * q + 1] * sr) * sc[1]);
             pk[1] = (int)pack_bf16x2((acc[i][j][4 * q + 2] * sr) * sc[2], (acc[i][j][4 * q + 3] * sr) * sc[3]);
@@ -303,29 +364,47 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 
 }  // namespace
 
-hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* wscale,
-                              const int* group_sizes, int G, int M, int K, int N, bool swiglu, uint16_t* out,
-                              uint16_t* preact, int* status, hipStream_t stream) {
+namespace {
+
+template <bool BF16>
+hipError_t launch_fwd_impl(const uint8_t* a, const float* ascale, const uint8_t* w, const float* wscale,
+                           const int* group_sizes, int G, int M, int K, int N, bool swiglu, uint16_t* out,
+                           uint16_t* preact, int* status, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const long long max_m_tiles = (M + BM - 1) / BM + G;
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
   if (swiglu) {
     const long long grid = max_m_tiles * ((N / 2) / 128);
-    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<true, 256>), dim3((unsigned)grid), dim3(kThreads),
-                       (lds_main<256>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
-                       swiglu ? preact : nullptr, status);
+    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<BF16, true, 256>), dim3((unsigned)grid), dim3(kThreads),
+                       (lds_main<256>() + table), stream, a, ascale, w, wscale, group_sizes, G, M, K, N, out, preact,
+                       status);
   } else if (N % 256 == 0) {
     const long long grid = max_m_tiles * (N / 256);
-    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 256>), dim3((unsigned)grid), dim3(kThreads),
-                       (lds_main<256>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
-                       swiglu ? preact : nullptr, status);
+    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<BF16, false, 256>), dim3((unsigned)grid), dim3(kThreads),
+                       (lds_main<256>() + table), stream, a, ascale, w, wscale, group_sizes, G, M, K, N, out, nullptr,
+                       status);
   } else {
     const long long grid = max_m_tiles * (N / 128);
-    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, 128>), dim3((unsigned)grid), dim3(kThreads),
-                       (lds_main<128>() + table), stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out,
-                       swiglu ? preact : nullptr, status);
+    hipLaunchKernelGGL((gmm_fp8_fwd_kernel<BF16, false, 128>), dim3((unsigned)grid), dim3(kThreads),
+                       (lds_main<128>() + table), stream, a, ascale, w, wscale, group_sizes, G, M, K, N, out, nullptr,
+                       status);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* wscale,
+                              const int* group_sizes, int G, int M, int K, int N, bool swiglu, uint16_t* out,
+                              uint16_t* preact, int* status, hipStream_t stream) {
+  return launch_fwd_impl<false>(aq, ascale, codes, wscale, group_sizes, G, M, K, N, swiglu, out,
+                                swiglu ? preact : nullptr, status, stream);
+}
+
+hipError_t launch_gmm_bf16_fwd(const uint16_t* lhs, const uint16_t* w, const int* group_sizes, int G, int M, int K,
+                               int N, bool swiglu, uint16_t* out, int* status, hipStream_t stream) {
+  return launch_fwd_impl<true>(reinterpret_cast<const uint8_t*>(lhs), nullptr, reinterpret_cast<const uint8_t*>(w),
+                               nullptr, group_sizes, G, M, K, N, swiglu, out, nullptr, status, stream);
 }
 
 }  // namespace fp8gmm

@@ -51,8 +51,9 @@ hipError_t launch_gmm_dswiglu_fp8(const uint16_t* dout, const uint8_t* codes, co
 hipError_t launch_gmm_bf16_dlhs(const uint16_t* dout, const uint16_t* w, const int* group_sizes, int G, int M, int K,
                                 int N, uint16_t* dlhs, int* status, hipStream_t stream);
 
+// bf16 measurement arm of the forward: the FP8 forward's kernel on bf16 operands.
 hipError_t launch_gmm_bf16_fwd(const uint16_t* lhs, const uint16_t* w, const int* group_sizes, int G, int M, int K,
-                               int N, uint16_t* out, int* status, hipStream_t stream);
+                               int N, bool swiglu, uint16_t* out, int* status, hipStream_t stream);
 
 // tgmm: workspace holds the transposed decoded operands and the scales.
 size_t tgmm_workspace_bytes(long long M, long long K, long long N, int G);

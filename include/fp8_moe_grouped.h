@@ -191,17 +191,23 @@ int dequantize_fp8_codes(const uint8_t* codes, const float* scale, int32_t G, in
                          void* stream);
 
 /*
- * bf16 measurement arm: the same group schedule and MFMA main loops with bf16
- * weights w[G, K, N] (for example the output of dequantize_fp8_codes) and no
- * activation quantization.  It is the bf16 GMM the FP8 forward is compared
- * against ([P1] Tests: kernel microbenchmark, the bf16 arm gets a weight
- * dequantized beforehand), and gmm_bf16_dlhs(dout, dequantize_fp8_codes(codes,
- * scale)) is bit-identical to gmm_dlhs_fp8(dout, codes, scale).
+ * bf16 measurement arm: the same group schedule, copy ring, wave layout and
+ * epilogues as the FP8 kernels with bf16 weights w[G, K, N] (for example the
+ * output of dequantize_fp8_codes) and no activation quantization.  It is the
+ * bf16 GMM the FP8 forward is compared against ([P1] Tests: kernel
+ * microbenchmark, the bf16 arm gets a weight dequantized beforehand), and
+ * gmm_bf16_dlhs(dout, dequantize_fp8_codes(codes, scale)) is bit-identical to
+ * gmm_dlhs_fp8(dout, codes, scale).
  *   gmm_bf16_fwd : out[r,n]  = bf16( sum_k lhs[r,k] * w[g,k,n] ),  out bf16 [M, N]
+ *   gmm_bf16_silu: with y[r,n] = sum_k lhs[r,k] * w[g,k,n] (f32) over N = 2*I
+ *                  columns [gate | up], out[r,i] = bf16( silu(y[r,i]) * y[r,I+i] ), out bf16 [M, I]
  *   gmm_bf16_dlhs: dlhs[r,k] = bf16( sum_n dout[r,n] * w[g,k,n] ), dlhs bf16 [M, K]
+ * K * N * 2 must be below 2^32 for the forward arms.
  */
 int gmm_bf16_fwd(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
                  int32_t G, void* out, int32_t* dev_status, void* stream);
+int gmm_bf16_silu(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
+                  int32_t G, void* out, int32_t* dev_status, void* stream);
 int gmm_bf16_dlhs(const void* dout, const void* w, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
                   int32_t G, void* dlhs, int32_t* dev_status, void* stream);
 

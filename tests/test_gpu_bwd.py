@@ -107,22 +107,43 @@ def test_dlhs_edges_and_stale_tail():
 
 # ---------------------------------------------------------------- bf16 forward arm
 
-def test_bf16_forward_arm():
+@pytest.mark.parametrize("config,N,silu", [(2, 2048, False), (0, 384, False), (1, 1536, True), (0, 256, True)])
+def test_bf16_forward_arm(config, N, silu):
+    """The bf16 arm (the FP8 forward's kernel on bf16 operands) against a
+    float64 matmul of the same seeded bf16 inputs: 256-column tiles (N = 2048),
+    128-column tiles (N = 384) and the SwiGLU epilogue."""
     import fp8_moe_grouped_amd as G
-    d = W.make(2, "wo")
-    w = G.dequantize_fp8_codes(dev(d["codes"]), dev(d["scale"]))
-    out = sentinel(d["M"], d["N"])
-    G.gmm_bf16_fwd(dev(d["lhs"]), w, dev(d["group_sizes"]), out=out)
+    d = W.make(config, "wo" if config == 2 else ("wi" if config == 1 else "fwd"))
+    K = d["K"]
+    w = W.bf16_weights(config, W.W_WO + 100, d["G"], K, N)
+    out = sentinel(d["M"], N // 2 if silu else N)
+    fn = G.gmm_bf16_silu if silu else G.gmm_bf16_fwd
+    fn(dev(d["lhs"]), dev(w), dev(d["group_sizes"]), out=out)
     torch.cuda.synchronize()
     got = bf16_np(out)
-    wd = F.bf16_to_f64(bf16_np(w))
+    wd = F.bf16_to_f64(w)
     x = F.bf16_to_f64(d["lhs"])
     lay = O.layout(d["group_sizes"], d["M"])
+    c_acc = K * 2.0 ** -24
     for g in range(d["G"]):
         a, b = lay.start[g], lay.end[g]
-        ref = x[a:b] @ wd[g]
+        if b == a:
+            continue
+        y = x[a:b] @ wd[g]
         absum = np.abs(x[a:b]) @ np.abs(wd[g])
-        check_bf16(got[a:b], ref, absum, np.zeros(b - a, int), d["K"] * 2.0 ** -24, "bf16 forward")
+        if not silu:
+            check_bf16(got[a:b], y, absum, np.zeros(b - a, int), c_acc, "bf16 forward")
+            continue
+        I = N // 2
+        gate, up = y[:, :I], y[:, I:]
+        eg, eu = c_acc * absum[:, :I] + 2.0 ** -21 * np.abs(gate), c_acc * absum[:, I:] + 2.0 ** -21 * np.abs(up)
+        with np.errstate(over="ignore"):
+            sig = 1.0 / (1.0 + np.exp(-gate))
+        extra = np.abs(sig * (1.0 + gate * (1.0 - sig))) * np.abs(up) * eg + np.abs(gate * sig) * eu \
+            + 2.0 ** -19 * np.abs(gate * sig * up)
+        check_bf16(got[a:b], O.swiglu(gate, up), np.zeros((b - a, I)), np.zeros(b - a, int), 0.0,
+                   "bf16 swiglu", extra_tol=extra)
+    assert np.all(got[lay.valid:] == SENTINEL)
 
 
 # ---------------------------------------------------------------- tgmm

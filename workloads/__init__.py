@@ -269,3 +269,73 @@ def ffn(key) -> dict:
                 wo_codes=wo_codes, wo_scale=wo_scale,
                 x=activations(c, FFN_X, M, H, valid, outlier_stream=FFN_X_OUT),
                 dy=gradients(c, FFN_DY, M, H, valid))
+
+
+def bf16_weights(config: int, stream: int, G: int, K: int, N: int, std: float = 0.02) -> np.ndarray:
+    """bf16 weights [G, K, N] ~ N(0, std) for the bf16 measurement arm."""
+    r = rng(config, stream)
+    out = np.empty((G, K, N), dtype=np.uint16)
+    for g in range(G):
+        out[g] = to_bf16_bits(r.standard_normal((K, N), dtype=np.float32) * np.float32(std))
+    return out
+
+
+#: The pages' GMM kernel microbenchmark at the trainer's per-device shapes: one
+#: call at full fill, 64 experts, 225,280 rows; wi 4096 -> 2x1024, wo 1024 -> 4096.
+MICRO = dict(G=64, M=225280, H=4096, I=1024)
+MICRO_CONFIG = 7
+MICRO_CHUNK = 8192
+
+
+def micro_group_sizes() -> np.ndarray:
+    """Full fill: every row valid; each row's expert uniform over the 64."""
+    r = rng(MICRO_CONFIG, ROUTING)
+    return np.bincount(r.integers(0, MICRO["G"], size=MICRO["M"]), minlength=MICRO["G"]).astype(np.int32)
+
+
+def _torch_gen(*key) -> torch.Generator:
+    """CPU torch generator seeded from a SeedSequence of ``key`` (the large
+    microbenchmark tensors use torch's CPU normal sampler, several times
+    faster than numpy's here; reproducible for a given torch version)."""
+    seed = int(np.random.SeedSequence(list(key)).generate_state(1, dtype=np.uint64)[0] >> 1)
+    return torch.Generator().manual_seed(seed)
+
+
+def micro_rows(stream: int, K: int, outliers: bool = True) -> np.ndarray:
+    """bf16 [225280, K]: activations N(0,1) with 1% of the entries (positions
+    drawn with replacement) x50, or with outliers=False gradients N(0, 1e-3)."""
+    M = MICRO["M"]
+    g = _torch_gen(MICRO_CONFIG, stream)
+    x = torch.randn((M, K), generator=g)
+    if outliers:
+        flat = x.view(-1)
+        idx = torch.randint(0, flat.numel(), (flat.numel() // 100,), generator=g)
+        flat[idx] = flat[idx] * 50.0
+    else:
+        x *= 1e-3
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def micro_weights(stream: int, G: int, K: int, N: int, std: float = 0.02):
+    """Weights ~ N(0, std) per expert as e4m3 codes + per-channel scales
+    (the recipe of ``weight_codes``), drawn with a torch CPU generator."""
+    g = _torch_gen(MICRO_CONFIG, stream)
+    codes = np.empty((G, K, N), dtype=np.uint8)
+    scale = np.empty((G, N), dtype=np.float32)
+    for e in range(G):
+        w = torch.randn((K, N), generator=g) * std
+        s = w.abs().amax(dim=0) / 448.0                    # f32, as weight_codes
+        q = (w / s[None, :]).clamp(-448.0, 448.0)
+        codes[e] = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        scale[e] = s.numpy()
+    return codes, scale
+
+
+def micro(op: str) -> dict:
+    """Inputs of one microbenchmark GMM: op ``wi`` (K=4096, N=2x1024, SwiGLU) or
+    ``wo`` (K=1024, N=4096), with e4m3 codes + scales as in config 0."""
+    G, H, I = MICRO["G"], MICRO["H"], MICRO["I"]
+    K, N, ws, xs = (H, 2 * I, W_WI, LHS_WI) if op == "wi" else (I, H, W_WO, LHS_WO)
+    codes, scale = micro_weights(ws, G, K, N)
+    return dict(G=G, M=MICRO["M"], K=K, N=N, group_sizes=micro_group_sizes(), codes=codes, scale=scale,
+                lhs=micro_rows(xs, K))
