@@ -422,3 +422,92 @@ def moe_ffn(x_bits, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes, dy_bits
     dwo = tgmm_quant(h_full, dy_bits, group_sizes, grad_fmt, tile_m)
     dwi = tgmm_quant(x_bits, dz_full, group_sizes, grad_fmt, tile_m)
     return FfnResult(fwd_wi, preact, h, fwd_wo, dsw, dx, dwo, dwi)
+
+
+# --------------------------------------------------------------------------- LHS-quant variants
+
+LHS_BLOCK = 512
+
+
+def gmm_fwd_variant(lhs_bits, codes, scale, group_sizes, *, block: int = 0, scale_bf16: bool = False,
+                    acc_bf16: bool = False, rhs_scale_first: bool = False, rows=None) -> FwdResult:
+    """The forward's LHS-quantization options kept as ops-level arguments for
+    benchmarks and tests (P1, Implementation: lhs_quant_block_size 512 or the
+    full K, lhs_f32_scale, rhs_scale_first; P2 review thread on the defaults:
+    a bf16 scale per 512-column block with a bf16 accumulator was the earlier
+    default).
+
+    * ``block``: columns per activation scale (0 = the full K).  Each row's K
+      axis is cut into blocks of ``block`` columns (the last may be shorter);
+      every block b gets ``s_b = f32(max(amax_b, 1e-12) / 448)``, rounded once
+      more to bf16 with ``scale_bf16``; its codes are ``e4m3(f32(x / s_b))``.
+    * block contribution ``t_b[n] = (P_b[n] * s_b) * scale[n]`` with
+      ``P_b = sum_{k in b} dec(q) dec(c)`` (exact); with ``rhs_scale_first``
+      the weight scale is applied first.  Both orders are the same real number:
+      the option only moves an f32 rounding, which float64 does not model.
+    * accumulation over blocks: float64 sum, or with ``acc_bf16`` a bf16
+      accumulator ``a <- bf16(f32(a + t_b))`` in block order.
+    * output ``bf16(sum)`` (``a`` itself with ``acc_bf16``).
+
+    ``FwdResult.act_scale`` holds the scales [R, n_blocks]; ``absum`` the sum
+    over blocks of ``s_b |scale| sum |dec q dec c|``.
+    """
+    lhs_bits = np.asarray(lhs_bits)
+    M, K = lhs_bits.shape
+    G, K2, N = codes.shape
+    assert K2 == K and scale.shape == (G, N)
+    bw = K if block <= 0 else block
+    edges = list(range(0, K, bw)) + [K]
+    nb = len(edges) - 1
+    lay = layout(group_sizes, M)
+    gid = lay.group_of_rows(M)
+    if rows is None:
+        rows = np.arange(lay.valid, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    assert np.all(gid[rows] >= 0), "requested rows must be valid rows"
+    R = len(rows)
+    y = np.zeros((R, N)); absum = np.zeros((R, N)); acc = np.zeros((R, N))
+    act_codes = np.zeros((R, K), np.uint8); act_scale = np.zeros((R, nb), np.float32)
+    for g in range(G):
+        sel = np.nonzero(gid[rows] == g)[0]
+        if len(sel) == 0:
+            continue
+        x = F.bf16_to_f32(lhs_bits[rows[sel]])
+        cd = F.decode(codes[g], F.E4M3)
+        sc = scale[g].astype(np.float64)
+        a = np.zeros((len(sel), N))
+        for b in range(nb):
+            k0, k1 = edges[b], edges[b + 1]
+            s = row_scales(x[:, k0:k1])
+            if scale_bf16:
+                s = F.round_to_bf16(s.astype(np.float64)).astype(np.float32)
+            q = quantize_rows(x[:, k0:k1], s)
+            qd = F.decode(q, F.E4M3)
+            t = (qd @ cd[k0:k1]) * s.astype(np.float64)[:, None] * sc[None, :]
+            absum[sel] += (np.abs(qd) @ np.abs(cd[k0:k1])) * s.astype(np.float64)[:, None] * np.abs(sc)[None, :]
+            y[sel] += t
+            if acc_bf16:
+                a = F.round_to_bf16(F.round_to_f32(a + t))
+            act_codes[sel, k0:k1] = q
+            act_scale[sel, b] = s
+        acc[sel] = a
+    out_f64 = acc if acc_bf16 else y
+    return FwdResult(rows, gid[rows], y, absum, F.f64_to_bf16_bits(out_f64), out_f64, act_codes, act_scale)
+
+
+def fake_qat_reference(lhs_bits, codes, scale, group_sizes, rows=None) -> np.ndarray:
+    """What the quantized forward approximates: the bf16 activations times the
+    weights code * scale, exactly (float64), per valid row (P1, Why: fake QAT
+    runs bf16 GMMs on dequantized weights)."""
+    lhs_bits = np.asarray(lhs_bits)
+    M = lhs_bits.shape[0]
+    lay = layout(group_sizes, M)
+    gid = lay.group_of_rows(M)
+    rows = np.arange(lay.valid, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    out = np.zeros((len(rows), codes.shape[2]))
+    for g in range(codes.shape[0]):
+        sel = np.nonzero(gid[rows] == g)[0]
+        if len(sel):
+            w = F.decode(codes[g], F.E4M3) * scale[g].astype(np.float64)[None, :]
+            out[sel] = F.bf16_to_f64(lhs_bits[rows[sel]]) @ w
+    return out

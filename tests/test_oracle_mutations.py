@@ -8,6 +8,7 @@ from oracle import gmm as O
 from tests import test_oracle_dswiglu as TD
 from tests import test_oracle_formats as TF
 from tests import test_oracle_gmm as TG
+from tests import test_oracle_variants as TV
 
 PINS = [
     TG.test_golden_worked_example,
@@ -33,6 +34,8 @@ PINS = [
     TD.test_dswiglu_closed_forms,
     TD.test_gmm_dswiglu_is_gradient_of_wo_loss,
     lambda: TD.test_moe_ffn_matches_straight_through_gradient(F.E4M3),
+    lambda: TV.test_variant_brute_force(True, True),
+    TV.test_equal_block_amax_reduces_to_full_k,
 ]
 
 
@@ -87,6 +90,7 @@ _real_col_scales = O.column_scales
 _real_fwd_rows = O._fwd_rows
 _real_dequant = O.dequantize
 _real_dswiglu = O.dswiglu
+_real_variant = O.gmm_fwd_variant
 _real_gmm_dswiglu = O.gmm_dswiglu
 
 
@@ -156,6 +160,10 @@ MUTATIONS = {
     "dswiglu gate and up gradients swapped": (O, "dswiglu", _mut_dswiglu_outputs_swapped),
     "dswiglu reads the pre-activation halves swapped": (O, "gmm_dswiglu", _mut_dswiglu_preact_halves_swapped),
     "dswiglu sign flipped": (O, "dswiglu", lambda d, g, u: tuple(-v for v in _real_dswiglu(d, g, u))),
+    "variant ignores the bf16 accumulator": (O, "gmm_fwd_variant",
+                                             lambda *a, **kw: _real_variant(*a, **{**kw, "acc_bf16": False})),
+    "variant ignores the bf16 scale": (O, "gmm_fwd_variant",
+                                       lambda *a, **kw: _real_variant(*a, **{**kw, "scale_bf16": False})),
 }
 
 

@@ -1,0 +1,152 @@
+"""Pins of the oracle's LHS-quantization variants (oracle/gmm.py:
+gmm_fwd_variant, fake_qat_reference).
+
+* reduction to the pinned forward: the full-K variant is gmm_fwd exactly, and
+  so are 512-column blocks when every block has the same amax;
+* exact-rational brute force on tiny shapes (tests/exact.py: Fraction
+  arithmetic, torch's float8 value table), with the scale and the accumulator
+  in bf16 or f32;
+* the fake-QAT reference against torch's own float8 dequantization;
+* the pages' ordering on synthetic data with outliers, read as distances to
+  a rollout that quantizes per row over the full K in f32: fake QAT is nearer
+  than a bf16 scale per 512 columns with a bf16 accumulator.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import gmm as O
+from tests import exact as X
+
+F32_1EM12 = Fraction(float(np.float32(1e-12)))
+
+
+def _bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _inputs(seed, G, M, K, N, sizes, outliers=False):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((M, K)).astype(np.float32) * 2
+    if outliers:
+        x[r.random((M, K)) < 0.01] *= 50
+    w = r.standard_normal((G, K, N)).astype(np.float32) * 0.02
+    scale = (np.abs(w).max(axis=1) / 448).astype(np.float32)
+    codes = torch.from_numpy(np.clip(w / scale[:, None, :], -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), codes, scale, \
+        np.array(sizes, np.int32)
+
+
+def test_full_k_variant_is_the_forward():
+    lhs, codes, scale, gs = _inputs(1, 3, 40, 96, 16, (10, 0, 25))
+    ref = O.gmm_fwd(lhs, codes, scale, gs)
+    for kw in (dict(), dict(block=96), dict(block=200), dict(rhs_scale_first=True), dict(acc_bf16=True)):
+        v = O.gmm_fwd_variant(lhs, codes, scale, gs, **kw)
+        assert np.array_equal(v.out, ref.out), kw
+        assert np.array_equal(v.act_codes, ref.act_codes)
+        assert np.array_equal(v.act_scale[:, 0], ref.act_scale)
+        np.testing.assert_allclose(v.y, ref.y, rtol=1e-15, atol=0)
+
+
+def test_equal_block_amax_reduces_to_full_k():
+    """Every 512-column block holds the row's amax: the block scales equal the
+    full-K scale, so the codes and (with f32 accumulation) the result agree."""
+    lhs, codes, scale, gs = _inputs(2, 2, 12, 1536, 8, (5, 7))
+    x = F.bf16_to_f32(lhs).copy()
+    amax = np.abs(x).max(axis=1) * 1.5
+    for b in range(3):
+        x[:, 512 * b + 7] = amax
+    lhs = _bits(x)
+    ref = O.gmm_fwd(lhs, codes, scale, gs)
+    v = O.gmm_fwd_variant(lhs, codes, scale, gs, block=512)
+    assert np.array_equal(v.act_codes, ref.act_codes)
+    assert np.all(v.act_scale == ref.act_scale[:, None])
+    np.testing.assert_allclose(v.y, ref.y, rtol=1e-12)
+    assert np.array_equal(v.out, ref.out)
+
+
+def _brute(lhs, codes, scale, sizes, block, scale_bf16, acc_bf16):
+    M, K = lhs.shape
+    G, _, N = codes.shape
+    _, tab = X.torch_table("e4m3")
+    out, scales, cds = {}, {}, {}
+    start = 0
+    for g in range(G):
+        end = min(start + max(int(sizes[g]), 0), M)
+        for r in range(start, end):
+            xs = [Fraction(float(v)) for v in F.bf16_to_f64(lhs[r])]
+            a = Fraction(0)
+            tot = Fraction(0)
+            sc_r, cd_r = [], []
+            for k0 in range(0, K, block):
+                blk = xs[k0:k0 + block]
+                s = X.to_f32(max(max(abs(v) for v in blk), F32_1EM12) / 448)
+                if scale_bf16:
+                    s = X.to_bf16(s)
+                q = [X.encode_brute(float(X.to_f32(v / s)), "e4m3") for v in blk]
+                cd_r += q
+                sc_r.append(s)
+                t = [sum(Fraction(float(tab[q[i]])) * Fraction(float(tab[codes[g, k0 + i, n]]))
+                         for i in range(len(blk))) * s * Fraction(float(scale[g, n])) for n in range(N)]
+                if acc_bf16:
+                    a = [X.to_bf16(X.to_f32((a[n] if isinstance(a, list) else 0) + t[n])) for n in range(N)]
+                else:
+                    tot = [(tot[n] if isinstance(tot, list) else 0) + t[n] for n in range(N)]
+            vals = a if acc_bf16 else [X.to_bf16(v) for v in tot]
+            out[r] = [X.bf16_bits_of(v) for v in vals]
+            scales[r], cds[r] = sc_r, cd_r
+        start = end
+    return out, scales, cds
+
+
+@pytest.mark.parametrize("scale_bf16,acc_bf16", [(False, False), (True, False), (False, True), (True, True)])
+def test_variant_brute_force(scale_bf16, acc_bf16):
+    lhs, codes, scale, gs = _inputs(3, 2, 9, 12, 3, (4, 5), outliers=True)
+    v = O.gmm_fwd_variant(lhs, codes, scale, gs, block=4, scale_bf16=scale_bf16, acc_bf16=acc_bf16)
+    out, scales, cds = _brute(lhs, codes, scale, gs, 4, scale_bf16, acc_bf16)
+    for i, r in enumerate(v.rows):
+        assert list(v.out[i]) == out[r], (r, list(v.out[i]), out[r])
+        assert [Fraction(float(s)) for s in v.act_scale[i]] == scales[r]
+        assert list(v.act_codes[i]) == cds[r]
+
+
+def test_fake_qat_reference_matches_torch_dequant():
+    lhs, codes, scale, gs = _inputs(4, 2, 20, 64, 8, (8, 9))
+    ref = O.fake_qat_reference(lhs, codes, scale, gs)
+    w = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64) * torch.from_numpy(scale).double()[:, None]
+    x = torch.from_numpy(lhs.view(np.int16)).view(torch.bfloat16).double()
+    exp = torch.cat([x[:8] @ w[0], x[8:17] @ w[1]]).numpy()
+    np.testing.assert_allclose(ref, exp, rtol=1e-13)
+
+
+def test_pages_ordering_against_the_rollout_reading():
+    """The pages compare the forward modes by their distance to the FP8
+    rollout's MoE kernel (P2 review thread on the defaults: full-K f32 scale
+    with f32 accumulation 0.0131, fake QAT 0.0468, a bf16 scale per 512
+    columns with a bf16 accumulator 0.0637; P1, Why: the native forward
+    matches what the rollout computes).  With the rollout read as per-row
+    full-K f32 quantization with f32 accumulation, the same ordering appears
+    on activations with 1% outliers x50 (K = 2048): fake QAT (the exact
+    product, rounded to bf16) is nearer than the block-512 bf16 mode.  Against
+    the exact product instead, 512-column blocks are the more accurate
+    quantization, so the ordering is a statement about matching the rollout,
+    not about accuracy."""
+    lhs, codes, scale, gs = _inputs(5, 2, 256, 2048, 128, (120, 136), outliers=True)
+    exact = O.fake_qat_reference(lhs, codes, scale, gs)
+    rollout = F.bf16_to_f64(O.gmm_fwd_variant(lhs, codes, scale, gs).out)
+
+    def dist(a, b):
+        return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+    fake_qat = F.bf16_to_f64(F.f64_to_bf16_bits(exact))
+    b512 = F.bf16_to_f64(O.gmm_fwd_variant(lhs, codes, scale, gs, block=512, scale_bf16=True, acc_bf16=True).out)
+    d_fake, d_b512 = dist(fake_qat, rollout), dist(b512, rollout)
+    assert 0 < d_fake < d_b512, (d_fake, d_b512)
+    e_full, e_b512 = dist(rollout, exact), dist(b512, exact)
+    assert e_b512 < e_full
+    print(f"distance to the full-K f32 forward: fake QAT {d_fake:.4f}, block-512 bf16 {d_b512:.4f}; "
+          f"to the exact product: full-K f32 {e_full:.4f}, block-512 bf16 {e_b512:.4f}")
