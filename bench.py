@@ -155,6 +155,34 @@ def cpu_baseline(d, seconds_target):
                       f"spread over the experts; {dt:.1f}s"}
 
 
+def lhs_quant_variants(G, stream, x, codes, scale, gs, mv):
+    """The forward's ops-level LHS-quantization variants on the dropless wi
+    input (K = 7168, N = 4096 without SwiGLU): quantizer + GEMM per call."""
+    import torch
+    M, K = x.shape
+    N = codes.shape[2]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = torch.empty(G.workspace_bytes(G.OP_FWD_VARIANT, M, K, N, codes.shape[0], 512), dtype=torch.uint8,
+                     device=x.device)
+    res = {"workload": "dropless wi input: G=32, 19661 valid rows, K=7168, N=4096 (no SwiGLU)"}
+    for name, kw in (("full_k_f32", {}), ("full_k_rhs_scale_first", dict(rhs_scale_first=True)),
+                     ("block512_f32", dict(lhs_block=512)),
+                     ("block512_bf16_scale_bf16_acc", dict(lhs_block=512, scale_bf16=True, acc_bf16=True))):
+        fn = lambda: G.gmm_fp8_fwd_variant(x, codes, scale, gs, out=out, workspace=ws, **kw)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(10):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = e[0].elapsed_time(e[1]) / 10
+        res[name] = {"ms": round(ms, 4), "tflops": round(2.0 * mv * K * N / (ms * 1e-3) / 1e12, 1)}
+    return res
+
+
 def pages_microbench(G, stream):
     """The pages' GMM kernel microbenchmark shape (one call at full fill, 64
     experts, 225,280 rows; wi 4096 -> 2x1024 with SwiGLU, wo 1024 -> 4096):
@@ -453,6 +481,7 @@ def main():
                  "pages_tpu7x": {"wi": 1.635, "wo": 1.731}}
         del w_wi
 
+    variants = lhs_quant_variants(G, stream, lhs_wi, codes_wi, scale_wi, gs, int(np.sum(d["gs"])))
     micro = None if args.no_micro else pages_microbench(G, stream)
     ffn = None if args.no_ffn else ffn_step(G, args, gs, lhs_wi, codes_wi, scale_wi, codes_wo, scale_wo, dout_wo,
                                             int(np.sum(d["gs"])), stream)
@@ -489,6 +518,7 @@ def main():
                           if ratio else None),
         "ffn_step": ffn,
         "pages_microbench": micro,
+        "lhs_quant_variants": variants,
     }
     print(json.dumps(line), flush=True)
 

@@ -26,7 +26,8 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
 DEV_SUM_CLAMPED, DEV_NEGATIVE_SIZE = 1, 2
 E4M3, E5M2 = 0, 1
-OP_FWD, OP_SILU, OP_DLHS, OP_TGMM, OP_BF16_FWD, OP_BF16_DLHS, OP_FFN_FWD, OP_FFN_BWD = 0, 1, 2, 3, 4, 5, 6, 7
+OP_FWD, OP_SILU, OP_DLHS, OP_TGMM, OP_BF16_FWD, OP_BF16_DLHS, OP_FFN_FWD, OP_FFN_BWD, OP_FWD_VARIANT = range(9)
+LHS_SCALE_BF16, ACC_BF16, RHS_SCALE_FIRST = 1, 2, 4
 GRAD_DTYPES = {"e4m3": E4M3, "e5m2": E5M2}
 
 
@@ -52,6 +53,7 @@ _SIGNATURES = {
     "quantize_rows_fp8": [_P, _P, _I64, _I64, _I32, _P, _P, _P],
     "gmm_fp8_fwd_q": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
     "gmm_silu_fp8_q": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P],
+    "gmm_fp8_fwd_variant": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P],
     "gmm_dswiglu_fp8": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
     "moe_ffn_fp8_fwd": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P, _P],
     "moe_ffn_fp8_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P,
@@ -189,6 +191,36 @@ def gmm_silu_fp8(lhs, codes, scale, group_sizes, *, out=None, preact=None, debug
     debug outputs when asked)."""
     return _fwd("gmm_silu_fp8", OP_SILU, lhs, codes, scale, group_sizes, out, debug, dev_status, workspace, True,
                 preact)
+
+
+def gmm_fp8_fwd_variant(lhs, codes, scale, group_sizes, *, lhs_block=0, scale_bf16=False, acc_bf16=False,
+                        rhs_scale_first=False, out=None, debug=False, dev_status=None, workspace=None):
+    """The FP8 forward with the ops-level LHS-quantization options: one scale
+    per row (lhs_block=0) or per 512 columns, optionally rounded to bf16, a
+    bf16 accumulator across the 512-column blocks, and the weight scale
+    applied first.  Returns bf16 [M, N] (with debug also the codes [M, K] and
+    the scales [M, nb])."""
+    _req(lhs, "lhs", torch.bfloat16, 2)
+    _req(codes, "codes", torch.uint8, 3)
+    _req(scale, "scale", torch.float32, 2)
+    _req(group_sizes, "group_sizes", torch.int32, 1)
+    dev = _same_device(lhs, codes, scale, group_sizes)
+    M, K = lhs.shape
+    G, K2, N = codes.shape
+    if K2 != K or tuple(scale.shape) != (G, N) or group_sizes.shape[0] != G:
+        raise ValueError("shape mismatch")
+    flags = (LHS_SCALE_BF16 if scale_bf16 else 0) | (ACC_BF16 if acc_bf16 else 0) | \
+        (RHS_SCALE_FIRST if rhs_scale_first else 0)
+    nb = -(-K // 512) if lhs_block == 512 else 1
+    out = _out(out, (M, N), torch.bfloat16, dev, "out")
+    dbg_codes = torch.empty((M, K), dtype=torch.uint8, device=dev) if debug else None
+    dbg_scale = torch.empty((M, nb), dtype=torch.float32, device=dev) if debug else None
+    ws, need = _workspace(OP_FWD_VARIANT, M, K, N, G, dev, tile_m=lhs_block, workspace=workspace)
+    with torch.cuda.device(dev):
+        _call("gmm_fp8_fwd_variant", _ptr(lhs), _ptr(codes), _ptr(scale), _ptr(group_sizes), M, K, N, G,
+              int(lhs_block), flags, _ptr(out), _ptr(dbg_codes), _ptr(dbg_scale), _ptr(ws), need, _ptr(dev_status),
+              _stream(dev))
+    return (out, dbg_codes, dbg_scale) if debug else out
 
 
 def quantize_rows_fp8(lhs, group_sizes, *, codes=None, scales=None):

@@ -26,6 +26,12 @@ int check_common(int64_t M, int64_t K, int64_t N, int32_t G) {
 // Forward workspace: activation codes [M, K] then row scales [M].
 size_t fwd_ws(int64_t M, int64_t K) { return align_up((size_t)M * K) + align_up((size_t)M * 4); }
 
+// Variant forward workspace: codes [M, K] then scales [M, ceil(K/512)] (or [M]).
+size_t variant_ws(int64_t M, int64_t K, int32_t lhs_block) {
+  const int64_t nb = lhs_block == 512 ? (K + 511) / 512 : 1;
+  return align_up((size_t)M * K) + align_up((size_t)M * nb * 4);
+}
+
 int fwd_common(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
                int64_t K, int64_t N, int32_t G, void* out, void* preact, uint8_t* dbg_codes, float* dbg_scale,
                void* ws, size_t ws_bytes, int32_t* dev_status, void* stream, bool swiglu) {
@@ -69,6 +75,35 @@ int gmm_silu_fp8(const void* lhs, const uint8_t* codes, const float* scale, cons
                  void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
   return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, preact, dbg_codes, dbg_scale, ws, ws_bytes,
                     dev_status, stream, true);
+}
+
+int gmm_fp8_fwd_variant(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                        int64_t M, int64_t K, int64_t N, int32_t G, int32_t lhs_block, int32_t flags, void* out,
+                        uint8_t* dbg_codes, float* dbg_scale, void* ws, size_t ws_bytes, int32_t* dev_status,
+                        void* stream) {
+  if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!lhs || !out)) return FP8GMM_ERR_NULL;
+  if (K > kMaxK || (lhs_block != 0 && lhs_block != 512)) return FP8GMM_ERR_UNSUPPORTED;
+  if (flags & ~(FP8GMM_LHS_SCALE_BF16 | FP8GMM_ACC_BF16 | FP8GMM_RHS_SCALE_FIRST)) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(lhs) || !aligned16(codes) || !aligned16(scale) || !aligned16(out) ||
+      (dbg_codes && !aligned16(dbg_codes)))
+    return FP8GMM_ERR_ALIGN;
+  const size_t need = variant_ws(M, K, lhs_block);
+  if (M > 0 && (!ws || ws_bytes < need)) return FP8GMM_ERR_WORKSPACE;
+  if (M == 0) return FP8GMM_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* aq = dbg_codes ? dbg_codes : static_cast<uint8_t*>(ws);
+  float* as = dbg_scale ? dbg_scale : reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)M * K));
+  const bool block = lhs_block == 512;
+  if (launch_quant_rows_e4m3_variant(static_cast<const uint16_t*>(lhs), group_sizes, G, (int)M, (int)K, block,
+                                     (flags & FP8GMM_LHS_SCALE_BF16) != 0, aq, as, s) != hipSuccess ||
+      launch_gmm_fp8_fwd_variant(aq, as, codes, scale, group_sizes, G, (int)M, (int)K, (int)N, block,
+                                 (flags & FP8GMM_ACC_BF16) != 0, (flags & FP8GMM_RHS_SCALE_FIRST) != 0,
+                                 static_cast<uint16_t*>(out), dev_status, s) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
 }
 
 int quantize_rows_fp8(const void* lhs, const int32_t* group_sizes, int64_t M, int64_t K, int32_t G,
@@ -317,6 +352,8 @@ size_t fp8gmm_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32
       return fwd_ws(M, K);
     case FP8GMM_OP_TGMM:
       return (tile_m == 512 && K % 256 == 0) ? tgmm_workspace_bytes(M, K, N, G) : 0;
+    case FP8GMM_OP_FWD_VARIANT:
+      return (tile_m == 0 || tile_m == 512) ? variant_ws(M, K, tile_m) : 0;
     case FP8GMM_OP_FFN_FWD:
       return check_ffn(M, K, N, G) == FP8GMM_OK ? ffn_fwd_ws(M, K, N) : 0;
     case FP8GMM_OP_FFN_BWD:

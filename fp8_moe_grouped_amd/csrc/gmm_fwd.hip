@@ -83,7 +83,15 @@ __device__ __forceinline__ v2i lds_read_tr16(const void* p) {
 // layout: aq / codes hold bf16 activations / weights, a stage still moves 64
 // bytes of every activation row (32 k) and 32 weight rows of 2*BN bytes, each
 // fragment takes two 32x32x16 bf16 MFMAs, and the epilogue has no scales.
-template <bool BF16, bool SWIGLU, int BN>
+// VAR (FP8, no SwiGLU, 128-column tiles): the ops-level LHS-quantization
+// variants ("MoE: native FP8 QAT for routed-expert GMMs", Implementation:
+// lhs_quant_block_size, rhs_scale_first; the bf16 accumulator of the earlier
+// default).  Bit 1: one activation scale per 512 columns (ascale is
+// [M, ceil(K/512)]); every 8 stages the block's accumulators are scaled and
+// folded into a running total.  Bit 2: that total is a bf16 accumulator
+// (rounded to bf16 after every fold).  Bit 4: the weight scale is applied
+// before the activation scale.
+template <bool BF16, bool SWIGLU, int BN, int VAR = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict__ ascale,
                         const uint8_t* __restrict__ codes, const float* __restrict__ wscale,
@@ -100,6 +108,8 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   constexpr int kLoads = kALoads + kBLoads;
   constexpr int kBRowsPerLoad = 1024 / kBRow;
   static_assert(!SWIGLU || BN == 256, "SwiGLU pairs 2 gate with 2 up fragments per wave");
+  static_assert(VAR == 0 || (!BF16 && !SWIGLU && BN == 128), "variants: FP8, plain epilogue, 128 columns");
+  constexpr bool kBlockQ = (VAR & 1) != 0, kAccBf16 = (VAR & 2) != 0, kRhsFirst = (VAR & 4) != 0;
   static_assert(kLoads * (kStages - 1) < 64, "outstanding copies fit vmcnt");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* t_start = reinterpret_cast<int*>(smem + lds_main<BN>());
@@ -221,6 +231,44 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 
   const int nk = K * kEl / BK;
 
+  // ---- variants: fold stage-block b's accumulators into the running total
+  v16f tot[MI][NJ];
+  if (kBlockQ) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
+  }
+  auto fold = [&](int blk) __attribute__((always_inline)) {
+    const int nb = (K + 511) >> 9;
+    const float* wsg = wscale + (size_t)g * N;
+    const int hl = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int ml = wm * 64 + i * 32 + (lane & 31);
+      const float sb = ml < rows ? ascale[(size_t)(row0 + ml) * nb + blk] : 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f sc = *reinterpret_cast<const v4f*>(wsg + nt * BN + wn * (BN / 2) + 32 * j + 8 * q + hl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = acc[i][j][4 * q + e];
+            const float t = kRhsFirst ? (a * sc[e]) * sb : (a * sb) * sc[e];
+            const float v = tot[i][j][4 * q + e] + t;
+            tot[i][j][4 * q + e] = kAccBf16 ? __builtin_bit_cast(float, pack_bf16x2(v, 0.f) << 16) : v;
+            acc[i][j][4 * q + e] = 0.f;
+          }
+        }
+    }
+  };
+  auto maybe_fold = [&](int k) __attribute__((always_inline)) {
+    if (kBlockQ && ((k & 7) == 7 || k + 1 == nk)) fold(k >> 3);
+  };
+
   // ---- prologue: stages 0..3 in flight, stage 0 landed and in registers
   const int pre = min(nk, kStages);
   for (int s = 0; s < pre; ++s)
@@ -281,11 +329,15 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   using W2 = std::integral_constant<int, 2>;
   auto slot = [&](int s) { return smem + (s % kStages) * kStageBytes; };
   int ks = 0;
-  for (; ks + kStages < nk; ++ks) step(ks, T_{}, T_{}, W2{}, slot(ks), slot(ks + 1));
-  if (ks + 3 < nk) { step(ks, F_{}, T_{}, W2{}, slot(ks), slot(ks + 1)); ++ks; }
-  if (ks + 2 < nk) { step(ks, F_{}, T_{}, W1{}, slot(ks), slot(ks + 1)); ++ks; }
-  if (ks + 1 < nk) { step(ks, F_{}, T_{}, W0{}, slot(ks), slot(ks + 1)); ++ks; }
+  for (; ks + kStages < nk; ++ks) {
+    step(ks, T_{}, T_{}, W2{}, slot(ks), slot(ks + 1));
+    maybe_fold(ks);
+  }
+  if (ks + 3 < nk) { step(ks, F_{}, T_{}, W2{}, slot(ks), slot(ks + 1)); maybe_fold(ks); ++ks; }
+  if (ks + 2 < nk) { step(ks, F_{}, T_{}, W1{}, slot(ks), slot(ks + 1)); maybe_fold(ks); ++ks; }
+  if (ks + 1 < nk) { step(ks, F_{}, T_{}, W0{}, slot(ks), slot(ks + 1)); maybe_fold(ks); ++ks; }
   step(ks, F_{}, F_{}, W0{}, slot(ks), slot(ks));
+  maybe_fold(ks);
 
   // ---- epilogue: lane owns row wm*64 + i*32 + lane%32 and, per fragment j,
   // columns tc(j) + 8*q + 4*(lane/32) + 0..3 for q = 0..3
@@ -297,7 +349,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
     const int ml = wm * 64 + i * 32 + (lane & 31);
     if (ml < rows) {
       const int row = row0 + ml;
-      const float sr = BF16 ? 1.f : ascale[row];
+      const float sr = (BF16 || kBlockQ) ? 1.f : ascale[row];
       if (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -352,9 +404,14 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
           for (int q = 0; q < 4; ++q) {
             const int c = nt * BN + wn * (BN / 2) + 32 * j + 8 * q + hl;
             const v4f sc = BF16 ? ones : *reinterpret_cast<const v4f*>(ws + c);
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = kBlockQ ? tot[i][j][4 * q + e]
+                             : (kRhsFirst ? (acc[i][j][4 * q + e] * sc[e]) * sr : (acc[i][j][4 * q + e] * sr) * sc[e]);
             v2i pk;
-            pk[0] = (int)pack_bf16x2((acc[i][j][4 * q] * sr) * sc[0], (acc[i][j][4 * q + 1] * sr) * sc[1]);
-            pk[1] = (int)pack_bf16x2((acc[i][j][4 * q + 2] * sr) * sc[2], (acc[i][j][4 * q + 3] * sr) * sc[3]);
+            pk[0] = (int)pack_bf16x2(v[0], v[1]);
+            pk[1] = (int)pack_bf16x2(v[2], v[3]);
             *reinterpret_cast<v2i*>(out + (size_t)row * N + c) = pk;
           }
       }
@@ -399,6 +456,31 @@ hipError_t launch_gmm_fp8_fwd(const uint8_t* aq, const float* ascale, const uint
                               uint16_t* preact, int* status, hipStream_t stream) {
   return launch_fwd_impl<false>(aq, ascale, codes, wscale, group_sizes, G, M, K, N, swiglu, out,
                                 swiglu ? preact : nullptr, status, stream);
+}
+
+hipError_t launch_gmm_fp8_fwd_variant(const uint8_t* aq, const float* ascale, const uint8_t* codes,
+                                      const float* wscale, const int* group_sizes, int G, int M, int K, int N,
+                                      bool block512, bool acc_bf16, bool rhs_first, uint16_t* out, int* status,
+                                      hipStream_t stream) {
+  const int var = (block512 ? 1 : 0) | (block512 && acc_bf16 ? 2 : 0) | (rhs_first ? 4 : 0);
+  if (var == 0)
+    return launch_fwd_impl<false>(aq, ascale, codes, wscale, group_sizes, G, M, K, N, false, out, nullptr, status,
+                                  stream);
+  if (M == 0) return hipSuccess;
+  const long long grid = ((M + BM - 1) / BM + G) * (N / 128);
+  const size_t lds = lds_main<128>() + sizeof(int) * (3 * (size_t)G + 1);
+#define VLAUNCH(V)                                                                                         \
+  hipLaunchKernelGGL((gmm_fp8_fwd_kernel<false, false, 128, V>), dim3((unsigned)grid), dim3(kThreads), lds,  \
+                     stream, aq, ascale, codes, wscale, group_sizes, G, M, K, N, out, nullptr, status)
+  switch (var) {
+    case 1: VLAUNCH(1); break;
+    case 3: VLAUNCH(3); break;
+    case 4: VLAUNCH(4); break;
+    case 5: VLAUNCH(5); break;
+    default: VLAUNCH(7); break;
+  }
+#undef VLAUNCH
+  return hipGetLastError();
 }
 
 hipError_t launch_gmm_bf16_fwd(const uint16_t* lhs, const uint16_t* w, const int* group_sizes, int G, int M, int K,

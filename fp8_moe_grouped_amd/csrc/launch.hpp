@@ -51,6 +51,15 @@ hipError_t launch_gmm_dswiglu_fp8(const uint16_t* dout, const uint8_t* codes, co
 hipError_t launch_gmm_bf16_dlhs(const uint16_t* dout, const uint16_t* w, const int* group_sizes, int G, int M, int K,
                                 int N, uint16_t* dlhs, int* status, hipStream_t stream);
 
+// Ops-level LHS-quantization variants: ascale holds [M, ceil(K/512)] block scales when block512.
+hipError_t launch_quant_rows_e4m3_variant(const uint16_t* lhs, const int* group_sizes, int G, int M, int K,
+                                          bool block512, bool scale_bf16, uint8_t* codes, float* scales,
+                                          hipStream_t stream);
+hipError_t launch_gmm_fp8_fwd_variant(const uint8_t* aq, const float* ascale, const uint8_t* codes,
+                                      const float* wscale, const int* group_sizes, int G, int M, int K, int N,
+                                      bool block512, bool acc_bf16, bool rhs_first, uint16_t* out, int* status,
+                                      hipStream_t stream);
+
 // bf16 measurement arm of the forward: the FP8 forward's kernel on bf16 operands.
 hipError_t launch_gmm_bf16_fwd(const uint16_t* lhs, const uint16_t* w, const int* group_sizes, int G, int M, int K,
                                int N, bool swiglu, uint16_t* out, int* status, hipStream_t stream);

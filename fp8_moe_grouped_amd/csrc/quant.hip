@@ -7,12 +7,24 @@
 // from HBM once: wave-wide amax -> f32 scale -> correctly rounded f32 quotient
 // -> saturating round-to-nearest-even e4m3fn code.  Rows at or past the valid
 // prefix (sum of group_sizes) are never read.
+//
+// The ops-level variants (same page, Implementation: lhs_quant_block_size 512
+// or the full K, and a bf16 scale) use one scale per 512 columns and/or round
+// the scale to bf16 before dividing.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace fp8gmm {
 
-template <int CPL>  // 16-byte chunks (8 bf16) per lane; covers K <= 512 * CPL
+__device__ __forceinline__ float round_to_bf16(float v) {
+  return __builtin_bit_cast(float, pack_bf16x2(v, 0.f) << 16);
+}
+
+// CPL: 16-byte chunks (8 bf16) per lane; covers K <= 512 * CPL.
+// BLOCK: one scale per 512 columns instead of per row (chunk iteration c of
+// the wave covers exactly columns [512c, 512c + 512)); scales are [M, nb].
+// SBF16: the f32 scale is rounded once more to bf16 (the bf16-scale option).
+template <int CPL, bool BLOCK = false, bool SBF16 = false>
 __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __restrict__ lhs,
                                                               const int* __restrict__ group_sizes, int G,
                                                               int M, int K, uint8_t* __restrict__ codes,
@@ -24,27 +36,35 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __
   const int nch = K >> 3;
   const v4i* src = reinterpret_cast<const v4i*>(lhs + (size_t)row * K);
   v4i x[CPL];
-  float amax = 0.0f;
+  float amax[BLOCK ? CPL : 1];
+#pragma unroll
+  for (int c = 0; c < (BLOCK ? CPL : 1); ++c) amax[c] = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int idx = lane + 64 * c;
     if (idx < nch) {
       x[c] = __builtin_nontemporal_load(src + idx);
+      float& am = amax[BLOCK ? c : 0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t w = (uint32_t)x[c][e];
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_lo(w)));
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_hi(w)));
+        am = __builtin_fmaxf(am, __builtin_fabsf(bf16_lo(w)));
+        am = __builtin_fmaxf(am, __builtin_fabsf(bf16_hi(w)));
       }
     }
   }
-  amax = wave_max(amax);
-  const float s = __builtin_fmaxf(amax, kAmaxFloor) / kE4M3Max;   // IEEE f32 division
+  float sc[BLOCK ? CPL : 1];
+#pragma unroll
+  for (int c = 0; c < (BLOCK ? CPL : 1); ++c) {
+    sc[c] = __builtin_fmaxf(wave_max(amax[c]), kAmaxFloor) / kE4M3Max;   // IEEE f32 division
+    if (SBF16) sc[c] = round_to_bf16(sc[c]);
+  }
   v2i* dst = reinterpret_cast<v2i*>(codes + (size_t)row * K);
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int idx = lane + 64 * c;
     if (idx < nch) {
+      const float s = sc[BLOCK ? c : 0];
       const uint32_t w0 = x[c][0], w1 = x[c][1], w2 = x[c][2], w3 = x[c][3];
       v2i q;
       q[0] = (int)cvt_e4m3x4(bf16_lo(w0) / s, bf16_hi(w0) / s, bf16_lo(w1) / s, bf16_hi(w1) / s);
@@ -52,7 +72,16 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __
       dst[idx] = q;
     }
   }
-  if (lane == 0) scales[row] = s;
+  if (lane == 0) {
+    if (BLOCK) {
+      const int nb = (K + 511) >> 9;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        if (c < nb) scales[(size_t)row * nb + c] = sc[c];
+    } else {
+      scales[row] = sc[0];
+    }
+  }
 }
 
 hipError_t launch_quant_rows_e4m3(const uint16_t* lhs, const int* group_sizes, int G, int M, int K,
@@ -71,6 +100,34 @@ hipError_t launch_quant_rows_e4m3(const uint16_t* lhs, const int* group_sizes, i
   else if (cpl <= 16) QLAUNCH(16);
   else if (cpl <= 32) QLAUNCH(32);
   else return hipErrorInvalidValue;
+#undef QLAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_e4m3_variant(const uint16_t* lhs, const int* group_sizes, int G, int M, int K,
+                                          bool block512, bool scale_bf16, uint8_t* codes, float* scales,
+                                          hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int nch = K / 8;
+  const int cpl = (nch + 63) / 64;
+  dim3 grid((M + 3) / 4), block(256);
+#define QLAUNCH(C, B, S)                                                                                     \
+  hipLaunchKernelGGL((quant_rows_e4m3_kernel<C, B, S>), grid, block, 0, stream, lhs, group_sizes, G, M, K,   \
+                     codes, scales)
+#define QPICK(B, S)                     \
+  if (cpl <= 1) QLAUNCH(1, B, S);       \
+  else if (cpl <= 2) QLAUNCH(2, B, S);  \
+  else if (cpl <= 4) QLAUNCH(4, B, S);  \
+  else if (cpl <= 8) QLAUNCH(8, B, S);  \
+  else if (cpl <= 16) QLAUNCH(16, B, S); \
+  else if (cpl <= 32) QLAUNCH(32, B, S); \
+  else return hipErrorInvalidValue;
+  if (block512) {
+    if (scale_bf16) { QPICK(true, true) } else { QPICK(true, false) }
+  } else {
+    if (scale_bf16) { QPICK(false, true) } else { QPICK(false, false) }
+  }
+#undef QPICK
 #undef QLAUNCH
   return hipGetLastError();
 }

@@ -68,6 +68,12 @@ extern "C" {
 #define FP8GMM_OP_BF16_DLHS 5
 #define FP8GMM_OP_FFN_FWD 6   /* moe_ffn_fp8_fwd: pass K = H, N = I */
 #define FP8GMM_OP_FFN_BWD 7   /* moe_ffn_fp8_bwd: pass K = H, N = I, tile_m = 512 */
+#define FP8GMM_OP_FWD_VARIANT 8 /* gmm_fp8_fwd_variant: pass lhs_block as tile_m */
+
+/* flags of gmm_fp8_fwd_variant */
+#define FP8GMM_LHS_SCALE_BF16 1   /* round each activation scale to bf16 */
+#define FP8GMM_ACC_BF16 2         /* bf16 accumulator across the 512-column blocks */
+#define FP8GMM_RHS_SCALE_FIRST 4  /* multiply by the weight scale before the activation scale */
 
 /*
  * gmm_fp8_fwd -- native FP8 forward GMM ([P1] Description: the forward GMMs
@@ -128,6 +134,27 @@ int gmm_fp8_fwd_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, 
 int gmm_silu_fp8_q(const uint8_t* aq, const float* ascale, const uint8_t* codes, const float* scale,
                    const int32_t* group_sizes, int64_t M, int64_t K, int64_t N, int32_t G, void* out, void* preact,
                    int32_t* dev_status, void* stream);
+
+/*
+ * gmm_fp8_fwd_variant -- the forward with the LHS-quantization options kept for
+ * benchmarks and tests ([P1] Implementation: lhs_quant_block_size 512 or the
+ * full K, lhs_f32_scale, rhs_scale_first; the bf16 scale per 512 columns with a
+ * bf16 accumulator was the earlier default).  lhs_block 0 = one scale per row
+ * over the full K, 512 = one scale per 512 columns (the last block may be
+ * shorter).  For block b of row r with P_b[r,n] = sum_{k in b} q[r,k] * codes[g,k,n]:
+ *   s_b      = f32( max(amax_b, 1e-12) / 448 ), then bf16(s_b) with FP8GMM_LHS_SCALE_BF16
+ *   q[r,k]   = e4m3fn( f32(lhs[r,k] / s_b) )
+ *   t_b[r,n] = (P_b * s_b) * scale[g,n]   ((P_b * scale[g,n]) * s_b with FP8GMM_RHS_SCALE_FIRST), f32
+ *   out      = bf16( sum_b t_b ), or with FP8GMM_ACC_BF16 (lhs_block 512 only) a <- bf16(a + t_b) in
+ *              block order and out = a
+ * lhs_block 0 with flags 0 is gmm_fp8_fwd bit for bit.  N must be a multiple of 128;
+ * no SwiGLU.  dbg_scale (or NULL) receives the scales, f32 [M, nb] with nb =
+ * ceil(K/512) or 1.  ws: fp8gmm_workspace_bytes(FP8GMM_OP_FWD_VARIANT, M, K, N, G, lhs_block).
+ */
+int gmm_fp8_fwd_variant(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                        int64_t M, int64_t K, int64_t N, int32_t G, int32_t lhs_block, int32_t flags, void* out,
+                        uint8_t* dbg_codes, float* dbg_scale, void* ws, size_t ws_bytes, int32_t* dev_status,
+                        void* stream);
 
 /*
  * gmm_dlhs_fp8 -- backward dLHS reading the FP8 codes ([P1] Description: the

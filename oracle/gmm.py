@@ -429,8 +429,13 @@ def moe_ffn(x_bits, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes, dy_bits
 LHS_BLOCK = 512
 
 
+@dataclass
+class VariantResult(FwdResult):
+    totals: np.ndarray = None   # [n_blocks, R, N]: the running total after each block (bf16 values with acc_bf16)
+
+
 def gmm_fwd_variant(lhs_bits, codes, scale, group_sizes, *, block: int = 0, scale_bf16: bool = False,
-                    acc_bf16: bool = False, rhs_scale_first: bool = False, rows=None) -> FwdResult:
+                    acc_bf16: bool = False, rhs_scale_first: bool = False, rows=None) -> VariantResult:
     """The forward's LHS-quantization options kept as ops-level arguments for
     benchmarks and tests (P1, Implementation: lhs_quant_block_size 512 or the
     full K, lhs_f32_scale, rhs_scale_first; P2 review thread on the defaults:
@@ -468,6 +473,7 @@ def gmm_fwd_variant(lhs_bits, codes, scale, group_sizes, *, block: int = 0, scal
     R = len(rows)
     y = np.zeros((R, N)); absum = np.zeros((R, N)); acc = np.zeros((R, N))
     act_codes = np.zeros((R, K), np.uint8); act_scale = np.zeros((R, nb), np.float32)
+    totals = np.zeros((nb, R, N))
     for g in range(G):
         sel = np.nonzero(gid[rows] == g)[0]
         if len(sel) == 0:
@@ -488,11 +494,13 @@ def gmm_fwd_variant(lhs_bits, codes, scale, group_sizes, *, block: int = 0, scal
             y[sel] += t
             if acc_bf16:
                 a = F.round_to_bf16(F.round_to_f32(a + t))
+            totals[b, sel] = a if acc_bf16 else y[sel]
             act_codes[sel, k0:k1] = q
             act_scale[sel, b] = s
         acc[sel] = a
     out_f64 = acc if acc_bf16 else y
-    return FwdResult(rows, gid[rows], y, absum, F.f64_to_bf16_bits(out_f64), out_f64, act_codes, act_scale)
+    return VariantResult(rows, gid[rows], y, absum, F.f64_to_bf16_bits(out_f64), out_f64, act_codes, act_scale,
+                         totals)
 
 
 def fake_qat_reference(lhs_bits, codes, scale, group_sizes, rows=None) -> np.ndarray:

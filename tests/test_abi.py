@@ -37,6 +37,8 @@ def test_header_macros_match_binding():
     assert vals["FP8GMM_E4M3"] == G.E4M3 and vals["FP8GMM_E5M2"] == G.E5M2
     assert vals["FP8GMM_OP_TGMM"] == G.OP_TGMM and vals["FP8GMM_DEV_NEGATIVE_SIZE"] == G.DEV_NEGATIVE_SIZE
     assert vals["FP8GMM_OP_FFN_FWD"] == G.OP_FFN_FWD and vals["FP8GMM_OP_FFN_BWD"] == G.OP_FFN_BWD
+    assert vals["FP8GMM_OP_FWD_VARIANT"] == G.OP_FWD_VARIANT and vals["FP8GMM_ACC_BF16"] == G.ACC_BF16
+    assert vals["FP8GMM_LHS_SCALE_BF16"] == G.LHS_SCALE_BF16 and vals["FP8GMM_RHS_SCALE_FIRST"] == G.RHS_SCALE_FIRST
 
 
 P = 0x10000          # fake, 16-byte aligned "device" address; never dereferenced
@@ -106,6 +108,22 @@ def test_dswiglu_and_ffn_validation():
     assert need >= L.fp8gmm_workspace_bytes(G.OP_TGMM, 64, 512, 512, 2, 512)
     assert bwd(wsb=need - 1) == G.ERR_WORKSPACE
     assert L.fp8gmm_workspace_bytes(G.OP_FFN_BWD, 64, 512, 256, 2, 256) == 0
+
+
+def test_variant_validation():
+    L = _lib()
+    v = lambda **kw: L.gmm_fp8_fwd_variant(P, P, P, P, kw.get("M", 256), kw.get("K", 1024), 256, 4,
+                                           kw.get("blk", 512), kw.get("flags", 3), kw.get("out", P), None, None,
+                                           kw.get("ws", P), kw.get("wsb", 1 << 30), None, None)
+    assert v(blk=256) == G.ERR_UNSUPPORTED
+    assert v(flags=8) == G.ERR_UNSUPPORTED
+    assert v(out=None) == G.ERR_NULL
+    assert v(out=BAD) == G.ERR_ALIGN
+    assert v(ws=None) == G.ERR_WORKSPACE
+    need = L.fp8gmm_workspace_bytes(G.OP_FWD_VARIANT, 256, 1024, 256, 4, 512)
+    assert need >= 256 * 1024 + 256 * 2 * 4
+    assert v(wsb=need - 1) == G.ERR_WORKSPACE
+    assert L.fp8gmm_workspace_bytes(G.OP_FWD_VARIANT, 256, 1024, 256, 4, 256) == 0
 
 
 def test_dlhs_and_tgmm_validation():
