@@ -519,3 +519,60 @@ def fake_qat_reference(lhs_bits, codes, scale, group_sizes, rows=None) -> np.nda
             w = F.decode(codes[g], F.E4M3) * scale[g].astype(np.float64)[None, :]
             out[sel] = F.bf16_to_f64(lhs_bits[rows[sel]]) @ w
     return out
+
+
+# --------------------------------------------------------------------------- dense backward quantization
+
+def tgmm_dense(lhs_bits, dout_bits, group_sizes, grad_fmt: str) -> TgmmResult:
+    """The buffer-wide backward quantization that the in-kernel tgmm replaces
+    (P3, What: three buffer-sized ops at the buffer's static size -- the
+    per-row lhs re-quantize, the drhs_dout *= lhs.scale multiply and the
+    per-N cotangent quantize; a stale row's Inf amax turns the weight
+    gradient into Inf * 0 = NaN).
+
+    Over every row of the static buffer, stale rows included:
+      sL[r]   = f32(max(amax_k |lhs[r,k]|, 1e-12) / 448),  qL = e4m3(f32(lhs / sL))
+      d'[r,n] = f32(dout[r,n] * sL[r])
+      sD[n]   = f32(max(amax_r |d'[r,n]|, 1e-12) / FMAX),  qD = grad(f32(d' / sD))
+    and per expert ``drhs[g,k,n] = sD[n] * sum_{r in g} dec(qL[r,k]) dec(qD[r,n])``
+    (exact integer sums, float64, rounded once to f32).  The amax ignores NaN
+    (IEEE maxNum, as a max instruction does); an expert without rows gets zeros.
+    ``sL`` of the result holds the row scales [M] (as [1, M]), ``sD`` the
+    column scales [1, N].
+    """
+    lhs_bits = np.asarray(lhs_bits); dout_bits = np.asarray(dout_bits)
+    M, K = lhs_bits.shape
+    N = dout_bits.shape[1]
+    G = len(group_sizes)
+    lay = layout(group_sizes, M)
+    x = F.bf16_to_f32(lhs_bits)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        amax_r = np.fmax.reduce(np.abs(x), axis=1) if K else np.zeros(M, np.float32)
+        sL = (np.maximum(np.nan_to_num(amax_r, nan=0.0, posinf=np.inf), AMAX_FLOOR) / E4M3_MAX).astype(np.float32)
+        qL = F.encode((x / sL[:, None]).astype(np.float32), F.E4M3)
+        dp = (F.bf16_to_f32(dout_bits) * sL[:, None]).astype(np.float32)
+        amax_n = np.fmax.reduce(np.abs(dp), axis=0)
+        sD = (np.maximum(np.nan_to_num(amax_n, nan=0.0, posinf=np.inf), AMAX_FLOOR)
+              / np.float32(F.FMAX[grad_fmt])).astype(np.float32)
+        qD = F.encode((dp / sD[None, :]).astype(np.float32), grad_fmt)
+    acc = np.zeros((G, K, N)); absum = np.zeros((G, K, N))
+    sh = _INT_SHIFT[F.E4M3] + _INT_SHIFT[grad_fmt]
+    for g in range(G):
+        a, b = int(lay.start[g]), int(lay.end[g])
+        if b == a:
+            continue
+        dl = F.decode(qL[a:b], F.E4M3)
+        dd = F.decode(qD[a:b], grad_fmt)
+        with np.errstate(invalid="ignore"):
+            iL = np.where(np.isfinite(dl), dl * 2.0 ** _INT_SHIFT[F.E4M3], 0).astype(np.int64)
+            iD = np.where(np.isfinite(dd), dd * 2.0 ** _INT_SHIFT[grad_fmt], 0).astype(np.int64)
+            s = (iL.T @ iD).astype(np.float64) * 2.0 ** -sh
+            sa = (np.abs(iL).T @ np.abs(iD)).astype(np.float64) * 2.0 ** -sh
+            # a NaN code anywhere in the expert's rows makes the sums NaN
+            nanL = ~np.isfinite(dl); nanD = ~np.isfinite(dd)
+            if nanL.any() or nanD.any():
+                bad = (nanL.astype(np.int64).T @ np.ones_like(iD) + np.ones_like(iL).T @ nanD.astype(np.int64)) > 0
+                s = np.where(bad, np.nan, s)
+            acc[g] = s * sD.astype(np.float64)[None, :]
+            absum[g] = sa * np.abs(sD.astype(np.float64))[None, :]
+    return TgmmResult(acc.astype(np.float32), acc, absum, [], sL[None, :], sD[None, :])

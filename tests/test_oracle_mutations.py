@@ -5,6 +5,7 @@ import pytest
 
 from oracle import formats as F
 from oracle import gmm as O
+from tests import test_oracle_dense as TE
 from tests import test_oracle_dswiglu as TD
 from tests import test_oracle_formats as TF
 from tests import test_oracle_gmm as TG
@@ -36,6 +37,8 @@ PINS = [
     lambda: TD.test_moe_ffn_matches_straight_through_gradient(F.E4M3),
     lambda: TV.test_variant_brute_force(True, True),
     TV.test_equal_block_amax_reduces_to_full_k,
+    lambda: TE.test_dense_brute_force(F.E5M2),
+    TE.test_stale_inf_poisons_dense_but_not_in_kernel,
 ]
 
 
@@ -91,6 +94,12 @@ _real_fwd_rows = O._fwd_rows
 _real_dequant = O.dequantize
 _real_dswiglu = O.dswiglu
 _real_variant = O.gmm_fwd_variant
+_real_dense = O.tgmm_dense
+
+
+def _mut_dense_valid_rows_only(lhs, dout, gs, fmt):
+    mv = O.layout(gs, np.asarray(lhs).shape[0]).valid
+    return _real_dense(np.asarray(lhs)[:mv], np.asarray(dout)[:mv], gs, fmt)
 _real_gmm_dswiglu = O.gmm_dswiglu
 
 
@@ -164,6 +173,7 @@ MUTATIONS = {
                                              lambda *a, **kw: _real_variant(*a, **{**kw, "acc_bf16": False})),
     "variant ignores the bf16 scale": (O, "gmm_fwd_variant",
                                        lambda *a, **kw: _real_variant(*a, **{**kw, "scale_bf16": False})),
+    "dense quantization skips the stale rows": (O, "tgmm_dense", _mut_dense_valid_rows_only),
 }
 
 
