@@ -155,6 +155,40 @@ def cpu_baseline(d, seconds_target):
                       f"spread over the experts; {dt:.1f}s"}
 
 
+def tgmm_dense_vs_in_kernel(G, stream, lhs, dout, gs, mv):
+    """The weight-gradient tgmm on the dropless buffer (32768 static rows,
+    19661 valid): in-kernel per-(tile, channel) quantization of the valid
+    rows (tgmm_quant) against the buffer-wide quantization baseline
+    (tgmm_dense_quant: every row of the buffer quantized, then the same
+    GEMM).  The garbage tail makes the baseline's gradient NaN; the timing is
+    what this records."""
+    import torch
+    M, K = lhs.shape
+    N = dout.shape[1]
+    Gn = gs.shape[0]
+    out = torch.empty((Gn, K, N), dtype=torch.float32, device=lhs.device)
+    ws_i = torch.empty(G.workspace_bytes(G.OP_TGMM, M, K, N, Gn, 512), dtype=torch.uint8, device=lhs.device)
+    ws_d = torch.empty(G.workspace_bytes(G.OP_TGMM_DENSE, M, K, N, Gn, 0), dtype=torch.uint8, device=lhs.device)
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(n):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / n
+
+    t_i = timed(lambda: G.tgmm_quant(lhs, dout, gs, "e5m2", 512, out=out, workspace=ws_i))
+    t_d = timed(lambda: G.tgmm_dense_quant(lhs, dout, gs, "e5m2", out=out, workspace=ws_d))
+    del ws_d
+    return {"workload": f"tgmm {K}x{N} e5m2 on the dropless buffer: {M} static rows, {mv} valid",
+            "in_kernel_ms": round(t_i, 4), "dense_ms": round(t_d, 4), "dense_over_in_kernel": round(t_d / t_i, 3)}
+
+
 def lhs_quant_variants(G, stream, x, codes, scale, gs, mv):
     """The forward's ops-level LHS-quantization variants on the dropless wi
     input (K = 7168, N = 4096 without SwiGLU): quantizer + GEMM per call."""
@@ -482,6 +516,7 @@ def main():
         del w_wi
 
     variants = lhs_quant_variants(G, stream, lhs_wi, codes_wi, scale_wi, gs, int(np.sum(d["gs"])))
+    dense = tgmm_dense_vs_in_kernel(G, stream, lhs_t, dout_t, gs, int(np.sum(d["gs"])))
     micro = None if args.no_micro else pages_microbench(G, stream)
     ffn = None if args.no_ffn else ffn_step(G, args, gs, lhs_wi, codes_wi, scale_wi, codes_wo, scale_wo, dout_wo,
                                             int(np.sum(d["gs"])), stream)
@@ -519,6 +554,7 @@ def main():
         "ffn_step": ffn,
         "pages_microbench": micro,
         "lhs_quant_variants": variants,
+        "tgmm_dense_baseline": dense,
     }
     print(json.dumps(line), flush=True)
 

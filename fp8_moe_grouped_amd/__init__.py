@@ -26,7 +26,8 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
 DEV_SUM_CLAMPED, DEV_NEGATIVE_SIZE = 1, 2
 E4M3, E5M2 = 0, 1
-OP_FWD, OP_SILU, OP_DLHS, OP_TGMM, OP_BF16_FWD, OP_BF16_DLHS, OP_FFN_FWD, OP_FFN_BWD, OP_FWD_VARIANT = range(9)
+(OP_FWD, OP_SILU, OP_DLHS, OP_TGMM, OP_BF16_FWD, OP_BF16_DLHS, OP_FFN_FWD, OP_FFN_BWD, OP_FWD_VARIANT,
+ OP_TGMM_DENSE) = range(10)
 LHS_SCALE_BF16, ACC_BF16, RHS_SCALE_FIRST = 1, 2, 4
 GRAD_DTYPES = {"e4m3": E4M3, "e5m2": E5M2}
 
@@ -50,6 +51,7 @@ _SIGNATURES = {
     "gmm_dlhs_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _SZ, _P, _P],
     "tgmm_quant": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P],
     "dequantize_fp8_codes": [_P, _P, _I32, _I64, _I64, _P, _P],
+    "tgmm_dense_quant": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P],
     "quantize_rows_fp8": [_P, _P, _I64, _I64, _I32, _P, _P, _P],
     "gmm_fp8_fwd_q": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
     "gmm_silu_fp8_q": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P],
@@ -418,6 +420,32 @@ def tgmm_quant(lhs, dout, group_sizes, grad_dtype="e5m2", tile_m=512, *, out=Non
         _call("tgmm_quant", _ptr(lhs), _ptr(dout), _ptr(group_sizes), M, K, N, G, gd, tile_m, _ptr(out),
               _ptr(dbg_sL), _ptr(dbg_sD), _ptr(ws), need, _ptr(dev_status), _stream(dev))
     return (out, dbg_sL, dbg_sD) if debug else out
+
+
+def tgmm_dense_quant(lhs, dout, group_sizes, grad_dtype="e5m2", *, out=None, debug=False, dev_status=None,
+                     workspace=None):
+    """The buffer-wide backward quantization baseline (every row of the
+    buffer, stale rows included): per-row lhs scale folded into dout, one
+    gradient scale per column; returns f32 [G, K, N] (with debug also the row
+    scales [M] and the column scales [N])."""
+    _req(lhs, "lhs", torch.bfloat16, 2)
+    _req(dout, "dout", torch.bfloat16, 2)
+    _req(group_sizes, "group_sizes", torch.int32, 1)
+    dev = _same_device(lhs, dout, group_sizes)
+    M, K = lhs.shape
+    M2, N = dout.shape
+    G = group_sizes.shape[0]
+    if M2 != M:
+        raise ValueError("lhs and dout must have the same number of rows")
+    gd = GRAD_DTYPES[grad_dtype] if isinstance(grad_dtype, str) else int(grad_dtype)
+    out = _out(out, (G, K, N), torch.float32, dev, "out")
+    srow = torch.empty((max(M, 1),), dtype=torch.float32, device=dev) if debug else None
+    scol = torch.empty((N,), dtype=torch.float32, device=dev) if debug else None
+    ws, need = _workspace(OP_TGMM_DENSE, M, K, N, G, dev, tile_m=0, workspace=workspace)
+    with torch.cuda.device(dev):
+        _call("tgmm_dense_quant", _ptr(lhs), _ptr(dout), _ptr(group_sizes), M, K, N, G, gd, _ptr(out), _ptr(srow),
+              _ptr(scol), _ptr(ws), need, _ptr(dev_status), _stream(dev))
+    return (out, srow, scol) if debug else out
 
 
 def dequantize_fp8_codes(codes, scale, *, out=None):

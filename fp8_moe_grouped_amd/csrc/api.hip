@@ -219,6 +219,26 @@ int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, 
   return FP8GMM_OK;
 }
 
+int tgmm_dense_quant(const void* lhs, const void* dout, const int32_t* group_sizes, int64_t M, int64_t K,
+                     int64_t N, int32_t G, int32_t grad_dtype, float* drhs, float* dbg_row_scale,
+                     float* dbg_col_scale, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  if (!group_sizes || !drhs) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!lhs || !dout)) return FP8GMM_ERR_NULL;
+  if (grad_dtype != FP8GMM_E4M3 && grad_dtype != FP8GMM_E5M2) return FP8GMM_ERR_UNSUPPORTED;
+  if (K % 256 != 0 || K > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(lhs) || !aligned16(dout) || !aligned16(drhs) || (dbg_col_scale && !aligned16(dbg_col_scale)))
+    return FP8GMM_ERR_ALIGN;
+  const size_t need = tgmm_dense_workspace_bytes(M, K, N, G);
+  if (need > 0 && (!ws || ws_bytes < need)) return FP8GMM_ERR_WORKSPACE;
+  if (launch_tgmm_dense(static_cast<const uint16_t*>(lhs), static_cast<const uint16_t*>(dout), group_sizes, G,
+                        (int)M, (int)K, (int)N, grad_dtype == FP8GMM_E5M2, drhs, dbg_row_scale, dbg_col_scale, ws,
+                        dev_status, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return FP8GMM_ERR_HIP;
+  return FP8GMM_OK;
+}
+
 static int bf16_fwd_common(const void* lhs, const void* w, const int32_t* group_sizes, int64_t M, int64_t K,
                            int64_t N, int32_t G, void* out, int32_t* dev_status, void* stream, bool swiglu) {
   if (!w || !group_sizes) return FP8GMM_ERR_NULL;
@@ -352,6 +372,8 @@ size_t fp8gmm_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32
       return fwd_ws(M, K);
     case FP8GMM_OP_TGMM:
       return (tile_m == 512 && K % 256 == 0) ? tgmm_workspace_bytes(M, K, N, G) : 0;
+    case FP8GMM_OP_TGMM_DENSE:
+      return (K % 256 == 0 && K <= kMaxK) ? tgmm_dense_workspace_bytes(M, K, N, G) : 0;
     case FP8GMM_OP_FWD_VARIANT:
       return (tile_m == 0 || tile_m == 512) ? variant_ws(M, K, tile_m) : 0;
     case FP8GMM_OP_FFN_FWD:

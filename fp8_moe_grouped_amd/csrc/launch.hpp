@@ -70,6 +70,14 @@ hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const in
                              int N, bool grad_e5m2, float* drhs, float* dbg_sl, float* dbg_sd, void* ws,
                              int* status, hipStream_t stream);
 
+// Buffer-wide baseline of the tgmm's operand quantization (every row of the buffer).
+size_t tgmm_dense_workspace_bytes(long long M, long long K, long long N, int G);
+hipError_t launch_tgmm_dense(const uint16_t* lhs, const uint16_t* dout, const int* group_sizes, int G, int M, int K,
+                             int N, bool grad_e5m2, float* drhs, float* dbg_srow, float* dbg_scol, void* ws,
+                             int* status, hipStream_t stream);
+hipError_t launch_quant_rows_e4m3_all(const uint16_t* lhs, int M, int K, uint8_t* codes, float* scales,
+                                      hipStream_t stream);
+
 hipError_t launch_dequant(const uint8_t* codes, const float* scale, int G, long long K, long long N, uint16_t* out,
                           hipStream_t stream);
 

@@ -24,13 +24,15 @@ __device__ __forceinline__ float round_to_bf16(float v) {
 // BLOCK: one scale per 512 columns instead of per row (chunk iteration c of
 // the wave covers exactly columns [512c, 512c + 512)); scales are [M, nb].
 // SBF16: the f32 scale is rounded once more to bf16 (the bf16-scale option).
-template <int CPL, bool BLOCK = false, bool SBF16 = false>
+// ALL: every row of the static buffer, stale rows included (the buffer-wide
+// baseline of the backward; nothing else quantizes stale rows).
+template <int CPL, bool BLOCK = false, bool SBF16 = false, bool ALL = false>
 __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __restrict__ lhs,
                                                               const int* __restrict__ group_sizes, int G,
                                                               int M, int K, uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int mv = valid_rows(group_sizes, G, M);
+  const int mv = ALL ? M : valid_rows(group_sizes, G, M);
   const int row = blockIdx.x * 4 + wave;
   if (row >= mv) return;
   const int nch = K >> 3;
@@ -128,6 +130,25 @@ hipError_t launch_quant_rows_e4m3_variant(const uint16_t* lhs, const int* group_
     if (scale_bf16) { QPICK(false, true) } else { QPICK(false, false) }
   }
 #undef QPICK
+#undef QLAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_e4m3_all(const uint16_t* lhs, int M, int K, uint8_t* codes, float* scales,
+                                      hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int cpl = (K / 8 + 63) / 64;
+  dim3 grid((M + 3) / 4), block(256);
+#define QLAUNCH(C)                                                                                           \
+  hipLaunchKernelGGL((quant_rows_e4m3_kernel<C, false, false, true>), grid, block, 0, stream, lhs, nullptr, 0, \
+                     M, K, codes, scales)
+  if (cpl <= 1) QLAUNCH(1);
+  else if (cpl <= 2) QLAUNCH(2);
+  else if (cpl <= 4) QLAUNCH(4);
+  else if (cpl <= 8) QLAUNCH(8);
+  else if (cpl <= 16) QLAUNCH(16);
+  else if (cpl <= 32) QLAUNCH(32);
+  else return hipErrorInvalidValue;
 #undef QLAUNCH
   return hipGetLastError();
 }

@@ -208,6 +208,130 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
   }
 }
 
+// ------------------------------------------------------------------ buffer-wide baseline
+//
+// The backward quantization the in-kernel path replaces ("MoE fp8 backward:
+// in-kernel drhs operand quantization + configurable gradient dtype", What:
+// three buffer-sized ops at the static size -- per-row lhs re-quantization,
+// dout *= the lhs row scale, per-column gradient quantization; a stale row's
+// Inf amax turns the weight gradient into Inf * 0 = NaN).  Every row of the
+// buffer is read, stale rows included; the contraction then reuses the GEMM
+// below with per-pair scales 1 (lhs) and the column scale (gradient).
+
+constexpr int kDenseRows = 128;   // rows per block of the column passes
+constexpr int kDenseCols = 2048;  // columns per block (8 per thread)
+
+// partial[rc][n] = max over the rows of chunk rc of |f32(dout[r,n] * srow[r])| (maxNum)
+__global__ __launch_bounds__(256) void dense_colmax_kernel(const uint16_t* __restrict__ dout,
+                                                           const float* __restrict__ srow, int M, int N,
+                                                           float* __restrict__ partial) {
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= N) return;
+  const int r0 = blockIdx.x * kDenseRows, r1 = min(M, r0 + kDenseRows);
+  float am[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am[e] = 0.f;
+#pragma unroll 4
+  for (int r = r0; r < r1; ++r) {
+    const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(dout + (size_t)r * N + c));
+    const float s = srow[r];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      am[2 * e] = __builtin_fmaxf(am[2 * e], __builtin_fabsf(bf16_lo((uint32_t)x[e]) * s));
+      am[2 * e + 1] = __builtin_fmaxf(am[2 * e + 1], __builtin_fabsf(bf16_hi((uint32_t)x[e]) * s));
+    }
+  }
+  float* dst = partial + (size_t)blockIdx.x * N + c;
+  *reinterpret_cast<v4f*>(dst) = (v4f){am[0], am[1], am[2], am[3]};
+  *reinterpret_cast<v4f*>(dst + 4) = (v4f){am[4], am[5], am[6], am[7]};
+}
+
+// scol[n] = f32(max(amax, 1e-12) / fmax) over the chunk maxima
+__global__ __launch_bounds__(256) void dense_colscale_kernel(const float* __restrict__ partial, int RC, int N,
+                                                             float fmax, float* __restrict__ scol) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float a = 0.f;
+  for (int rc = 0; rc < RC; ++rc) a = __builtin_fmaxf(a, partial[(size_t)rc * N + n]);
+  scol[n] = __builtin_fmaxf(a, kAmaxFloor) / fmax;
+}
+
+// qD[r, n] = grad( f32( f32(dout[r,n] * srow[r]) / scol[n] ) ) for every row of the buffer
+template <bool GRAD_E5M2>
+__global__ __launch_bounds__(256) void dense_quant_kernel(const uint16_t* __restrict__ dout,
+                                                          const float* __restrict__ srow,
+                                                          const float* __restrict__ scol, int M, int N,
+                                                          uint8_t* __restrict__ qD) {
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= N) return;
+  const int r0 = blockIdx.x * kDenseRows, r1 = min(M, r0 + kDenseRows);
+  const v4f sa = *reinterpret_cast<const v4f*>(scol + c), sb = *reinterpret_cast<const v4f*>(scol + c + 4);
+  const float sc[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+#pragma unroll 4
+  for (int r = r0; r < r1; ++r) {
+    const v4i x = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(dout + (size_t)r * N + c));
+    const float s = srow[r];
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[2 * e] = (bf16_lo((uint32_t)x[e]) * s) / sc[2 * e];
+      q[2 * e + 1] = (bf16_hi((uint32_t)x[e]) * s) / sc[2 * e + 1];
+    }
+    v2i w;
+    if (GRAD_E5M2) {
+      w[0] = (int)cvt_e5m2x4(q[0], q[1], q[2], q[3]);
+      w[1] = (int)cvt_e5m2x4(q[4], q[5], q[6], q[7]);
+    } else {
+      w[0] = (int)cvt_e4m3x4(q[0], q[1], q[2], q[3]);
+      w[1] = (int)cvt_e4m3x4(q[4], q[5], q[6], q[7]);
+    }
+    *reinterpret_cast<v2i*>(qD + (size_t)r * N + c) = w;
+  }
+}
+
+// The valid rows' codes of the buffer-wide operands into the GEMM's pair
+// slabs (zeros up to the 64-row chunk), with per-pair scales 1 for the lhs
+// (its row scales are inside the gradient) and scol for the gradient.
+__global__ __launch_bounds__(kThreads) void dense_gather_kernel(const uint8_t* __restrict__ qLd,
+                                                                const uint8_t* __restrict__ qDd,
+                                                                const float* __restrict__ scol,
+                                                                const int* __restrict__ group_sizes, int G, int M,
+                                                                int K, int N, uint8_t* __restrict__ ql,
+                                                                uint8_t* __restrict__ qd, float* __restrict__ sl,
+                                                                float* __restrict__ sd, int* status) {
+  __shared__ int g_start[kMaxGroups], g_end[kMaxGroups], p_base[kMaxGroups + 1];
+  PairTable pt{g_start, g_end, p_base};
+  build_pair_table(group_sizes, G, M, pt, blockIdx.y == 0 ? status : nullptr);
+  __syncthreads();
+  const int p = blockIdx.x;
+  if (p >= p_base[G]) return;
+  const int g = pair_group(pt, G, p);
+  int r0, r1;
+  pair_rows(pt, g, p, r0, r1);
+  const int R = r1 - r0;
+  const int Rpad = (R + kChunk - 1) / kChunk * kChunk;
+  const int kc = K / kPrepCols;
+  const bool is_l = (int)blockIdx.y < kc;
+  const int cols = is_l ? K : N;
+  const int c0 = (is_l ? (int)blockIdx.y : (int)blockIdx.y - kc) * kPrepCols;
+  const int tid = threadIdx.x, cg = tid & 7, rr = tid >> 3;
+  const uint8_t* src = (is_l ? qLd : qDd) + c0 + cg * 8;
+  uint8_t* dst = (is_l ? ql + (size_t)p * kTileM * K : qd + (size_t)p * kTileM * N) + c0 + cg * 8;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = rr + 32 * i;
+    if (r < Rpad) {
+      v2i w = (v2i){0, 0};
+      if (r < R) w = *reinterpret_cast<const v2i*>(src + (size_t)(r0 + r) * cols);
+      *reinterpret_cast<v2i*>(dst + (size_t)r * cols) = w;
+    }
+  }
+  if (tid < kPrepCols) {
+    if (is_l) sl[(size_t)p * K + c0 + tid] = 1.0f;
+    else sd[(size_t)p * N + c0 + tid] = scol[c0 + tid];
+  }
+}
+
 // ------------------------------------------------------------------ gemm
 
 constexpr int BMK = 256;                        // drhs rows (k) per block
@@ -471,6 +595,69 @@ size_t tgmm_workspace_bytes(long long M, long long K, long long N, int G) {
          al((size_t)tmax * N * 4);
 }
 
+namespace {
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+hipError_t launch_tgmm_gemm(const uint8_t* ql, const uint8_t* qd, const float* sl, const float* sd,
+                            const int* group_sizes, int G, int M, int K, int N, bool grad_e5m2, float* drhs,
+                            hipStream_t stream) {
+  const size_t lds = kLdsG + sizeof(int) * (4 * (size_t)G + 1);
+  const long long items = (long long)G * (K / BMK) * (N / BNN);
+  const dim3 grid((unsigned)std::min<long long>(items, device_cu_count()));   // one resident block per CU
+  if (grad_e5m2)
+    hipLaunchKernelGGL(tgmm_gemm_kernel<true>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G, M,
+                       K, N, drhs);
+  else
+    hipLaunchKernelGGL(tgmm_gemm_kernel<false>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G,
+                       M, K, N, drhs);
+  return hipGetLastError();
+}
+}  // namespace
+
+size_t tgmm_dense_workspace_bytes(long long M, long long K, long long N, int G) {
+  const long long rc = (M + kDenseRows - 1) / kDenseRows;
+  return tgmm_workspace_bytes(M, K, N, G) + al256((size_t)M * K) + al256((size_t)M * 4) + al256((size_t)M * N) +
+         al256((size_t)rc * N * 4) + al256((size_t)N * 4);
+}
+
+hipError_t launch_tgmm_dense(const uint16_t* lhs, const uint16_t* dout, const int* group_sizes, int G, int M, int K,
+                             int N, bool grad_e5m2, float* drhs, float* dbg_srow, float* dbg_scol, void* ws,
+                             int* status, hipStream_t stream) {
+  const long long tmax = (M + kTileM - 1) / kTileM + G - 1;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* ql = base;
+  uint8_t* qd = base + al256((size_t)tmax * kTileM * K);
+  float* sl = reinterpret_cast<float*>(qd + al256((size_t)tmax * kTileM * N));
+  float* sd = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sl) + al256((size_t)tmax * K * 4));
+  uint8_t* dense = base + tgmm_workspace_bytes(M, K, N, G);
+  const int rc = (M + kDenseRows - 1) / kDenseRows;
+  uint8_t* qLd = dense;
+  float* srow = reinterpret_cast<float*>(qLd + al256((size_t)M * K));
+  uint8_t* qDd = reinterpret_cast<uint8_t*>(srow) + al256((size_t)M * 4);
+  float* partial = reinterpret_cast<float*>(qDd + al256((size_t)M * N));
+  float* scol = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(partial) + al256((size_t)rc * N * 4));
+  if (dbg_srow) srow = dbg_srow;
+  if (dbg_scol) scol = dbg_scol;
+  if (M > 0) {
+    hipError_t e = launch_quant_rows_e4m3_all(lhs, M, K, qLd, srow, stream);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)rc, (unsigned)((N + kDenseCols - 1) / kDenseCols));
+    hipLaunchKernelGGL(dense_colmax_kernel, grid, dim3(256), 0, stream, dout, srow, M, N, partial);
+    hipLaunchKernelGGL(dense_colscale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, partial, rc, N,
+                       grad_e5m2 ? kE5M2Max : kE4M3Max, scol);
+    if (grad_e5m2)
+      hipLaunchKernelGGL(dense_quant_kernel<true>, grid, dim3(256), 0, stream, dout, srow, scol, M, N, qDd);
+    else
+      hipLaunchKernelGGL(dense_quant_kernel<false>, grid, dim3(256), 0, stream, dout, srow, scol, M, N, qDd);
+    if (tmax > 0)
+      hipLaunchKernelGGL(dense_gather_kernel, dim3((unsigned)tmax, (unsigned)(K / kPrepCols + N / kPrepCols)),
+                         dim3(kThreads), 0, stream, qLd, qDd, scol, group_sizes, G, M, K, N, ql, qd, sl, sd, status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_tgmm_gemm(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
+}
+
 hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const int* group_sizes, int G, int M, int K,
                              int N, bool grad_e5m2, float* drhs, float* dbg_sl, float* dbg_sd, void* ws,
                              int* status, hipStream_t stream) {
@@ -495,16 +682,7 @@ hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t lds = kLdsG + sizeof(int) * (4 * (size_t)G + 1);
-  const long long items = (long long)G * (K / BMK) * (N / BNN);
-  const dim3 grid((unsigned)std::min<long long>(items, device_cu_count()));   // one resident block per CU
-  if (grad_e5m2)
-    hipLaunchKernelGGL(tgmm_gemm_kernel<true>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G, M,
-                       K, N, drhs);
-  else
-    hipLaunchKernelGGL(tgmm_gemm_kernel<false>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G,
-                       M, K, N, drhs);
-  return hipGetLastError();
+  return launch_tgmm_gemm(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
 }
 
 }  // namespace fp8gmm

@@ -69,6 +69,7 @@ extern "C" {
 #define FP8GMM_OP_FFN_FWD 6   /* moe_ffn_fp8_fwd: pass K = H, N = I */
 #define FP8GMM_OP_FFN_BWD 7   /* moe_ffn_fp8_bwd: pass K = H, N = I, tile_m = 512 */
 #define FP8GMM_OP_FWD_VARIANT 8 /* gmm_fp8_fwd_variant: pass lhs_block as tile_m */
+#define FP8GMM_OP_TGMM_DENSE 9  /* tgmm_dense_quant */
 
 /* flags of gmm_fp8_fwd_variant */
 #define FP8GMM_LHS_SCALE_BF16 1   /* round each activation scale to bf16 */
@@ -208,6 +209,26 @@ int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, 
 int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
                int32_t G, int32_t grad_dtype, int32_t tile_m, float* drhs, float* dbg_sL, float* dbg_sD, void* ws,
                size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * tgmm_dense_quant -- the buffer-wide backward quantization that tgmm_quant
+ * replaces, kept as a measurement baseline ([P3] What: three buffer-sized ops
+ * at the static size -- the per-row lhs re-quantization, the dout *= lhs
+ * row-scale multiply and the per-column gradient quantization -- and a stale
+ * row's Inf amax turns the weight gradient into Inf * 0 = NaN).  Over EVERY
+ * row r < M of the buffer, stale rows included (amax ignores NaN):
+ *   sL[r]   = f32(max(max_k |lhs[r,k]|, 1e-12) / 448),   qL = e4m3(f32(lhs / sL))
+ *   d'[r,n] = f32(dout[r,n] * sL[r])
+ *   sD[n]   = f32(max(max_r |d'[r,n]|, 1e-12) / FMAX),   qD = grad(f32(d' / sD))
+ *   drhs[g,k,n] = f32( sD[n] * sum_{r in rows(g)} qL[r,k] * qD[r,n] )
+ * so an Inf in any stale row makes every non-empty expert's gradient NaN;
+ * experts without rows get zeros.  Arguments as tgmm_quant (no tile_m);
+ * dbg_row_scale f32 [M] / dbg_col_scale f32 [N] (or NULL) receive sL / sD.
+ * ws: fp8gmm_workspace_bytes(FP8GMM_OP_TGMM_DENSE, M, K, N, G, 0) bytes.
+ */
+int tgmm_dense_quant(const void* lhs, const void* dout, const int32_t* group_sizes, int64_t M, int64_t K,
+                     int64_t N, int32_t G, int32_t grad_dtype, float* drhs, float* dbg_row_scale,
+                     float* dbg_col_scale, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
 /*
  * dequantize_fp8_codes -- out[g,k,n] = bf16( f32(codes[g,k,n] * scale[g,n]) )

@@ -523,7 +523,7 @@ def fake_qat_reference(lhs_bits, codes, scale, group_sizes, rows=None) -> np.nda
 
 # --------------------------------------------------------------------------- dense backward quantization
 
-def tgmm_dense(lhs_bits, dout_bits, group_sizes, grad_fmt: str) -> TgmmResult:
+def tgmm_dense(lhs_bits, dout_bits, group_sizes, grad_fmt: str, k_cols=None, n_cols=None) -> TgmmResult:
     """The buffer-wide backward quantization that the in-kernel tgmm replaces
     (P3, What: three buffer-sized ops at the buffer's static size -- the
     per-row lhs re-quantize, the drhs_dout *= lhs.scale multiply and the
@@ -538,7 +538,9 @@ def tgmm_dense(lhs_bits, dout_bits, group_sizes, grad_fmt: str) -> TgmmResult:
     (exact integer sums, float64, rounded once to f32).  The amax ignores NaN
     (IEEE maxNum, as a max instruction does); an expert without rows gets zeros.
     ``sL`` of the result holds the row scales [M] (as [1, M]), ``sD`` the
-    column scales [1, N].
+    column scales [1, N].  ``k_cols``/``n_cols`` restrict the output to some
+    columns: the row scales still span all of K, and a gradient column's
+    scale depends on that column alone, so the restriction is exact.
     """
     lhs_bits = np.asarray(lhs_bits); dout_bits = np.asarray(dout_bits)
     M, K = lhs_bits.shape
@@ -549,12 +551,16 @@ def tgmm_dense(lhs_bits, dout_bits, group_sizes, grad_fmt: str) -> TgmmResult:
     with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
         amax_r = np.fmax.reduce(np.abs(x), axis=1) if K else np.zeros(M, np.float32)
         sL = (np.maximum(np.nan_to_num(amax_r, nan=0.0, posinf=np.inf), AMAX_FLOOR) / E4M3_MAX).astype(np.float32)
+        if k_cols is not None:
+            x = x[:, np.asarray(k_cols)]
         qL = F.encode((x / sL[:, None]).astype(np.float32), F.E4M3)
-        dp = (F.bf16_to_f32(dout_bits) * sL[:, None]).astype(np.float32)
+        d = F.bf16_to_f32(dout_bits if n_cols is None else np.asarray(dout_bits)[:, np.asarray(n_cols)])
+        dp = (d * sL[:, None]).astype(np.float32)
         amax_n = np.fmax.reduce(np.abs(dp), axis=0)
         sD = (np.maximum(np.nan_to_num(amax_n, nan=0.0, posinf=np.inf), AMAX_FLOOR)
               / np.float32(F.FMAX[grad_fmt])).astype(np.float32)
         qD = F.encode((dp / sD[None, :]).astype(np.float32), grad_fmt)
+    K, N = x.shape[1], d.shape[1]
     acc = np.zeros((G, K, N)); absum = np.zeros((G, K, N))
     sh = _INT_SHIFT[F.E4M3] + _INT_SHIFT[grad_fmt]
     for g in range(G):

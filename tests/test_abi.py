@@ -126,6 +126,21 @@ def test_variant_validation():
     assert L.fp8gmm_workspace_bytes(G.OP_FWD_VARIANT, 256, 1024, 256, 4, 256) == 0
 
 
+def test_dense_validation():
+    L = _lib()
+    dn = lambda **kw: L.tgmm_dense_quant(kw.get("lhs", P), P, P, kw.get("M", 1024), kw.get("K", 256), 128, 3,
+                                         kw.get("gd", G.E5M2), kw.get("drhs", P), None, None, kw.get("ws", P),
+                                         kw.get("wsb", 1 << 30), None, None)
+    assert dn(lhs=None) == G.ERR_NULL
+    assert dn(drhs=None) == G.ERR_NULL
+    assert dn(gd=5) == G.ERR_UNSUPPORTED
+    assert dn(K=128) == G.ERR_UNSUPPORTED
+    assert dn(ws=None) == G.ERR_WORKSPACE
+    need = L.fp8gmm_workspace_bytes(G.OP_TGMM_DENSE, 1024, 256, 128, 3, 0)
+    assert need > L.fp8gmm_workspace_bytes(G.OP_TGMM, 1024, 256, 128, 3, 512) + 1024 * (256 + 128)
+    assert dn(wsb=need - 1) == G.ERR_WORKSPACE
+
+
 def test_dlhs_and_tgmm_validation():
     L = _lib()
     assert L.gmm_dlhs_fp8(None, P, P, P, 8, 128, 128, 2, P, P, 1 << 20, None, None) == G.ERR_NULL
