@@ -40,16 +40,16 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes over this bench
-# (profiles/bench_kernels_dropless32_ffn_micro.md), scaled by a plain 1 GiB copy: FETCH_SIZE x 2.0,
+# (profiles/bench_kernels_all_sections.md), scaled by a plain 1 GiB copy: FETCH_SIZE x 2.0,
 # WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
 # were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "39a9afbc65585920", 2254, 77),
-    "wo_gemm": ("gmm_fwd.hip", "39a9afbc65585920", 847, 271),
-    "wi_dlhs": ("dlhs.hip", "394beec51dc067f6", 2288, 269),
-    "wo_dlhs": ("dlhs.hip", "394beec51dc067f6", 1263, 77),
-    "tgmm": ("tgmm.hip", "1d29ad0648d0f7b7", 346 + 1450, 188 + 1926),
-    "dequant": ("dequant.hip", "ef163e21ecb4c831", 455, 976),
+    "wi_gemm": ("gmm_fwd.hip", "957212819c7f3502", 2261, 77),
+    "wo_gemm": ("gmm_fwd.hip", "957212819c7f3502", 849, 270),
+    "wi_dlhs": ("dlhs.hip", "b62e3797d9e441f6", 2289, 269),
+    "wo_dlhs": ("dlhs.hip", "b62e3797d9e441f6", 1263, 77),
+    "tgmm": ("tgmm.hip", "ba9d449f75ad065a", 346 + 1450, 188 + 1926),
+    "dequant": ("dequant.hip", "1066860594ec257a", 455, 976),
 }
 
 
@@ -362,6 +362,8 @@ def main():
     ap.add_argument("--no-bf16-arm", action="store_true")
     ap.add_argument("--no-ffn", action="store_true", help="skip the MoE FFN forward + backward measurement")
     ap.add_argument("--no-micro", action="store_true", help="skip the pages' microbenchmark shape")
+    ap.add_argument("--no-variants", action="store_true", help="skip the LHS-quantization variants")
+    ap.add_argument("--no-dense", action="store_true", help="skip the buffer-wide tgmm baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy (read MIB, write MIB) three times; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE hardware counters to bytes")
@@ -515,8 +517,9 @@ def main():
                  "pages_tpu7x": {"wi": 1.635, "wo": 1.731}}
         del w_wi
 
-    variants = lhs_quant_variants(G, stream, lhs_wi, codes_wi, scale_wi, gs, int(np.sum(d["gs"])))
-    dense = tgmm_dense_vs_in_kernel(G, stream, lhs_t, dout_t, gs, int(np.sum(d["gs"])))
+    mv = int(np.sum(d["gs"]))
+    variants = None if args.no_variants else lhs_quant_variants(G, stream, lhs_wi, codes_wi, scale_wi, gs, mv)
+    dense = None if args.no_dense else tgmm_dense_vs_in_kernel(G, stream, lhs_t, dout_t, gs, mv)
     micro = None if args.no_micro else pages_microbench(G, stream)
     ffn = None if args.no_ffn else ffn_step(G, args, gs, lhs_wi, codes_wi, scale_wi, codes_wo, scale_wo, dout_wo,
                                             int(np.sum(d["gs"])), stream)
