@@ -246,14 +246,23 @@ __global__ __launch_bounds__(256) void dense_colmax_kernel(const uint16_t* __res
   *reinterpret_cast<v4f*>(dst + 4) = (v4f){am[4], am[5], am[6], am[7]};
 }
 
-// scol[n] = f32(max(amax, 1e-12) / fmax) over the chunk maxima
+// scol[n] = f32(max(amax, 1e-12) / fmax) over the chunk maxima: a block takes
+// 32 columns, its eight 32-thread groups stride over the chunks, LDS combines.
 __global__ __launch_bounds__(256) void dense_colscale_kernel(const float* __restrict__ partial, int RC, int N,
                                                              float fmax, float* __restrict__ scol) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float red[8][32];
+  const int c = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int n = blockIdx.x * 32 + c;
   float a = 0.f;
-  for (int rc = 0; rc < RC; ++rc) a = __builtin_fmaxf(a, partial[(size_t)rc * N + n]);
-  scol[n] = __builtin_fmaxf(a, kAmaxFloor) / fmax;
+  if (n < N)
+    for (int rc = grp; rc < RC; rc += 8) a = __builtin_fmaxf(a, partial[(size_t)rc * N + n]);
+  red[grp][c] = a;
+  __syncthreads();
+  if (grp == 0 && n < N) {
+#pragma unroll
+    for (int i = 1; i < 8; ++i) a = __builtin_fmaxf(a, red[i][c]);
+    scol[n] = __builtin_fmaxf(a, kAmaxFloor) / fmax;
+  }
 }
 
 // qD[r, n] = grad( f32( f32(dout[r,n] * srow[r]) / scol[n] ) ) for every row of the buffer
@@ -643,7 +652,7 @@ hipError_t launch_tgmm_dense(const uint16_t* lhs, const uint16_t* dout, const in
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)rc, (unsigned)((N + kDenseCols - 1) / kDenseCols));
     hipLaunchKernelGGL(dense_colmax_kernel, grid, dim3(256), 0, stream, dout, srow, M, N, partial);
-    hipLaunchKernelGGL(dense_colscale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, partial, rc, N,
+    hipLaunchKernelGGL(dense_colscale_kernel, dim3((unsigned)((N + 31) / 32)), dim3(256), 0, stream, partial, rc, N,
                        grad_e5m2 ? kE5M2Max : kE4M3Max, scol);
     if (grad_e5m2)
       hipLaunchKernelGGL(dense_quant_kernel<true>, grid, dim3(256), 0, stream, dout, srow, scol, M, N, qDd);
