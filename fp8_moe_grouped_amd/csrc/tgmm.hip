@@ -43,7 +43,8 @@ namespace {
 
 constexpr int kTileM = 512;       // rows per gm-tile (the only supported value)
 constexpr int kPrepCols = 64;     // columns per prep block
-constexpr int kChunk = 64;        // contraction rows per GEMM stage
+constexpr int kSub = 32;          // contraction rows per MFMA sub-step (slabs are padded to this)
+constexpr int kChunk = 128;       // contraction rows per GEMM stage (1 to 4 sub-steps)
 constexpr int kThreads = 256;
 
 // Pair table from group_sizes, built by wave 0 into LDS: for pair p (in
@@ -116,21 +117,23 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
   __shared__ int g_start[kMaxGroups], g_end[kMaxGroups], p_base[kMaxGroups + 1];
   __shared__ float red[4][kPrepCols];
   PairTable pt{g_start, g_end, p_base};
-  build_pair_table(group_sizes, G, M, pt, blockIdx.y == 0 ? status : nullptr);
+  // blockIdx.x = 64-column chunk (fastest, so that blocks dispatched together
+  // read neighbouring strips of the same rows), blockIdx.y = pair
+  build_pair_table(group_sizes, G, M, pt, blockIdx.x == 0 ? status : nullptr);
   __syncthreads();
-  const int p = blockIdx.x;
+  const int p = blockIdx.y;
   if (p >= p_base[G]) return;
   const int g = pair_group(pt, G, p);
   int r0, r1;
   pair_rows(pt, g, p, r0, r1);
   const int R = r1 - r0;
-  const int Rpad = (R + kChunk - 1) / kChunk * kChunk;
+  const int Rpad = (R + kSub - 1) / kSub * kSub;
 
   // which operand and columns
   const int kc = K / kPrepCols;
-  const bool is_l = (int)blockIdx.y < kc;
+  const bool is_l = (int)blockIdx.x < kc;
   const int cols = is_l ? K : N;
-  const int c0 = (is_l ? (int)blockIdx.y : (int)blockIdx.y - kc) * kPrepCols;
+  const int c0 = (is_l ? (int)blockIdx.x : (int)blockIdx.x - kc) * kPrepCols;
   const uint16_t* src = is_l ? lhs : dout;
   const float fmax = is_l ? kE4M3Max : (GRAD_E5M2 ? kE5M2Max : kE4M3Max);
 
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void dense_gather_kernel(const uint8_t* _
   int r0, r1;
   pair_rows(pt, g, p, r0, r1);
   const int R = r1 - r0;
-  const int Rpad = (R + kChunk - 1) / kChunk * kChunk;
+  const int Rpad = (R + kSub - 1) / kSub * kSub;
   const int kc = K / kPrepCols;
   const bool is_l = (int)blockIdx.y < kc;
   const int cols = is_l ? K : N;
@@ -346,10 +349,10 @@ __global__ __launch_bounds__(kThreads) void dense_gather_kernel(const uint8_t* _
 constexpr int BMK = 256;                        // drhs rows (k) per block
 constexpr int BNN = 128;                        // drhs columns (n) per block
 constexpr int kGThreads = 512;                  // 8 waves: 4 along k x 2 along n, 64 x 64 each
-constexpr int kAStage = kChunk * BMK;           // qL codes [64 rows][256 k]
-constexpr int kBStage = kChunk * BNN;           // qD codes [64 rows][128 n]
-constexpr int kStageG = kAStage + kBStage;      // 24 KiB
-constexpr int kStagesG = 5;
+constexpr int kAStage = kChunk * BMK;           // qL codes [128 rows][256 k]
+constexpr int kBStage = kChunk * BNN;           // qD codes [128 rows][128 n]
+constexpr int kStageG = kAStage + kBStage;      // 48 KiB
+constexpr int kStagesG = 3;
 constexpr int kLdsG = kStagesG * kStageG;
 constexpr int kALoadsG = kAStage / (8 * 1024);  // 1 KB wave-wide loads per wave per stage
 constexpr int kBLoadsG = kBStage / (8 * 1024);
@@ -380,12 +383,13 @@ __device__ __forceinline__ v4i widen8(const v2i& c) {
   return o;
 }
 
-// One 64-row stage: optionally start the copy of a later stage into `wr`,
-// then read this stage's operands from `rd` and run its 32 MFMAs per wave.
+// One 128-row stage: optionally start the copy of a later stage into `wr`,
+// then read this stage's operands from `rd` and run NS 32-row sub-steps of
+// 16 MFMAs per wave.
 // `wr` and `rd` are distinct ring slots; marking them __restrict__ lets the
 // compiler see that the reads cannot depend on the copy just issued, so it
 // adds no wait for it (the kernel's own wait + barrier order the ring).
-template <bool GRAD_E5M2>
+template <bool GRAD_E5M2, int NS>
 __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, bool copy,
                                            BufRsrc ra, BufRsrc rb, const uint32_t* va, const uint32_t* vb,
                                            uint32_t soa, uint32_t sob, int wave, const int* a_rd, const int* b_rd,
@@ -397,7 +401,7 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
     for (int j = 0; j < kBLoadsG; ++j) dma16(rb, wr + kAStage + (kBLoadsG * wave + j) * 1024, vb[j], sob);
   }
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     v4i bo[4], ao[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bo[j] = widen8<GRAD_E5M2>(lds_read_tr8(rd + b_rd[j] + s * 32 * BNN));
@@ -421,7 +425,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   int* g_start = reinterpret_cast<int*>(smem + kLdsG);
   int* g_end = g_start + G;
   int* p_base = g_end + G;
-  int* g_chunks = p_base + G + 1;     // 64-row chunks of each expert (all its pairs)
+  int* g_chunks = p_base + G + 1;     // 128-row stages of each expert (all its pairs)
   PairTable pt{g_start, g_end, p_base};
   build_pair_table(group_sizes, G, M, pt, nullptr);
   __syncthreads();
@@ -472,7 +476,12 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   for (int j = 0; j < 4; ++j) b_rd[j] = kAStage + d_slot(rbase, wn * 4 + j) + 8 * (Lg & 1);
 
   // ---- copy side: the next (item, pair, chunk) to copy, stages run ahead of the compute side
-  int ii = blockIdx.x, ig = 0, ikt = 0, int_ = 0, ip = 0, ip1 = 0, ic = 0, inc = 0;
+  int ii = blockIdx.x, ig = 0, ikt = 0, int_ = 0, ip = 0, ip1 = 0, ic = 0, inc = 0, irows = 0;
+  auto pair_pad_rows = [&](int g, int p) {
+    int r0, r1;
+    pair_rows(pt, g, p, r0, r1);
+    return __builtin_amdgcn_readfirstlane((r1 - r0 + kSub - 1) / kSub * kSub);
+  };
   auto seek = [&]() {   // first item at or after ii that has rows
     while (ii < total && g_chunks[ii / per_g] == 0) ii += stride;
     if (ii < total) {
@@ -484,12 +493,16 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
       ip1 = __builtin_amdgcn_readfirstlane(p_base[ig + 1]);
       ic = 0;
       inc = __builtin_amdgcn_readfirstlane(nchunks(ig, ip));
+      irows = pair_pad_rows(ig, ip);
     }
   };
   int tI = 0;
   // copy parameters of the next chunk (ii, ip, ic)
-  auto copy_rsrc_a = [&]() { return make_rsrc(ql + (size_t)ip * kTileM * K, (uint32_t)kTileM * (uint32_t)K); };
-  auto copy_rsrc_b = [&]() { return make_rsrc(qd + (size_t)ip * kTileM * N, (uint32_t)kTileM * (uint32_t)N); };
+  // the copy of a pair's last stage may run past its rows (padded with zero
+  // codes to a multiple of 32): the buffer range ends there, so those loads
+  // return zeros and the stage's MFMAs add nothing for them
+  auto copy_rsrc_a = [&]() { return make_rsrc(ql + (size_t)ip * kTileM * K, (uint32_t)irows * (uint32_t)K); };
+  auto copy_rsrc_b = [&]() { return make_rsrc(qd + (size_t)ip * kTileM * N, (uint32_t)irows * (uint32_t)N); };
   uint32_t va_i[kALoadsG], vb_i[kBLoadsG];      // copy offsets with the item's column origin
   auto set_item_offsets = [&]() {
 #pragma unroll
@@ -507,6 +520,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
         set_item_offsets();
       } else {
         inc = __builtin_amdgcn_readfirstlane(nchunks(ig, ip));
+        irows = pair_pad_rows(ig, ip);
       }
     }
   };
@@ -555,17 +569,16 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
         // it may still be in flight; other loads and stores only make the
         // wait stricter); stage tC-1's buffer is free for the next copy
         const int pending = tI - 1 - tC;
-        static_assert(kStagesG <= 6, "one wait per possible count below");
-        if (pending >= 4) wait_vmem_lds<4 * kLoadsG>();
-        else if (pending == 3) wait_vmem_lds<3 * kLoadsG>();
-        else if (pending == 2) wait_vmem_lds<2 * kLoadsG>();
-        else if (pending == 1) wait_vmem_lds<kLoadsG>();
+        static_assert(kStagesG == 3, "one wait per possible count below");
+        if (pending >= 1) wait_vmem_lds<kLoadsG>();
         else wait_vmem_lds<0>();
         barrier_only();
         const bool copy = ii < total;
-        tgmm_stage<GRAD_E5M2>(smem + (tI % kStagesG) * kStageG, smem + (tC % kStagesG) * kStageG, copy,
-                              copy_rsrc_a(), copy_rsrc_b(), va_i, vb_i, (uint32_t)ic * kChunk * (uint32_t)K,
-                              (uint32_t)ic * kChunk * (uint32_t)N, wave, a_rd, b_rd, part);
+        uint8_t* wr = smem + (tI % kStagesG) * kStageG;
+        const uint8_t* rd = smem + (tC % kStagesG) * kStageG;
+        const uint32_t soa = (uint32_t)ic * kChunk * (uint32_t)K, sob = (uint32_t)ic * kChunk * (uint32_t)N;
+        tgmm_stage<GRAD_E5M2, kChunk / kSub>(wr, rd, copy, copy_rsrc_a(), copy_rsrc_b(), va_i, vb_i, soa, sob, wave,
+                                             a_rd, b_rd, part);
         if (copy) advance();
       }
       // pair complete: total += partial * sL[k] * sD[n]
@@ -681,7 +694,7 @@ hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const in
   if (dbg_sl) sl = dbg_sl;
   if (dbg_sd) sd = dbg_sd;
   if (tmax > 0 && M > 0) {
-    dim3 grid((unsigned)tmax, (unsigned)(K / kPrepCols + N / kPrepCols));
+    dim3 grid((unsigned)(K / kPrepCols + N / kPrepCols), (unsigned)tmax);
     if (grad_e5m2)
       hipLaunchKernelGGL(tgmm_prep_kernel<true>, grid, dim3(kThreads), 0, stream, lhs, dout, group_sizes, G, M, K,
                          N, ql, qd, sl, sd, status);
