@@ -77,6 +77,7 @@ struct Cfg {
   static constexpr int kWLoads = kWBytes / 1024 / 8;
   static constexpr int kLoads = kALoads + kWLoads + (FROM_CODES ? 1 : 0);
   static_assert(kLoads < 64, "outstanding copies fit vmcnt");
+  static_assert(kLds + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
 };
 
 // 16-byte chunk swizzles, conflict-free for the operand reads (16 lanes read
@@ -359,11 +360,16 @@ hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const fl
   if (M == 0) return hipSuccess;
   const long long max_m_tiles = (M + BM - 1) / BM + G;
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
-  if (FROM_CODES && K % 256 == 0) {
-    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 256, DSWIGLU>), dim3((unsigned)(max_m_tiles * (K / 256))),
-                       dim3(kThreads), (Cfg<FROM_CODES, 256>::kLds + table), stream, dout, codes, scale, wbf16,
-                       group_sizes, G, M, K, N, preact, dlhs, status);
-  } else {
+  // bf16 weights always take 128-column tiles (a 256-column bf16 ring does not fit the LDS)
+  if constexpr (FROM_CODES) {
+    if (K % 256 == 0) {
+      hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 256, DSWIGLU>), dim3((unsigned)(max_m_tiles * (K / 256))),
+                         dim3(kThreads), (Cfg<FROM_CODES, 256>::kLds + table), stream, dout, codes, scale, wbf16,
+                         group_sizes, G, M, K, N, preact, dlhs, status);
+      return hipGetLastError();
+    }
+  }
+  {
     hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 128, DSWIGLU>), dim3((unsigned)(max_m_tiles * (K / 128))),
                        dim3(kThreads), (Cfg<FROM_CODES, 128>::kLds + table), stream, dout, codes, scale, wbf16,
                        group_sizes, G, M, K, N, preact, dlhs, status);

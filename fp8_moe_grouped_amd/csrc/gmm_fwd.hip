@@ -53,6 +53,7 @@ template <int BN>
 constexpr int stage_bytes() { return BM * BK + BK * BN; }
 template <int BN>
 constexpr int lds_main() { return kStages * stage_bytes<BN>(); }
+static_assert(lds_main<256>() + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
 
 // 16-byte chunk swizzles: 16 lanes reading 16 consecutive activation rows at
 // one chunk, and two transposing-read groups (8 weight rows each, adjacent

@@ -354,6 +354,7 @@ constexpr int kBStage = kChunk * BNN;           // qD codes [128 rows][128 n]
 constexpr int kStageG = kAStage + kBStage;      // 48 KiB
 constexpr int kStagesG = 3;
 constexpr int kLdsG = kStagesG * kStageG;
+static_assert(kLdsG + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
 constexpr int kALoadsG = kAStage / (8 * 1024);  // 1 KB wave-wide loads per wave per stage
 constexpr int kBLoadsG = kBStage / (8 * 1024);
 constexpr int kLoadsG = kALoadsG + kBLoadsG;
@@ -425,7 +426,6 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   int* g_start = reinterpret_cast<int*>(smem + kLdsG);
   int* g_end = g_start + G;
   int* p_base = g_end + G;
-  int* g_chunks = p_base + G + 1;     // 128-row stages of each expert (all its pairs)
   PairTable pt{g_start, g_end, p_base};
   build_pair_table(group_sizes, G, M, pt, nullptr);
   __syncthreads();
@@ -434,12 +434,6 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
     pair_rows(pt, g, p, r0, r1);
     return (r1 - r0 + kChunk - 1) / kChunk;
   };
-  for (int g = threadIdx.x; g < G; g += kGThreads) {
-    int c = 0;
-    for (int p = p_base[g]; p < p_base[g + 1]; ++p) c += nchunks(g, p);
-    g_chunks[g] = c;
-  }
-  __syncthreads();
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -483,7 +477,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
     return __builtin_amdgcn_readfirstlane((r1 - r0 + kSub - 1) / kSub * kSub);
   };
   auto seek = [&]() {   // first item at or after ii that has rows
-    while (ii < total && g_chunks[ii / per_g] == 0) ii += stride;
+    while (ii < total && p_base[ii / per_g + 1] == p_base[ii / per_g]) ii += stride;   // expert without rows
     if (ii < total) {
       ig = __builtin_amdgcn_readfirstlane(ii / per_g);
       const int rem = ii % per_g;
@@ -623,7 +617,7 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 hipError_t launch_tgmm_gemm(const uint8_t* ql, const uint8_t* qd, const float* sl, const float* sd,
                             const int* group_sizes, int G, int M, int K, int N, bool grad_e5m2, float* drhs,
                             hipStream_t stream) {
-  const size_t lds = kLdsG + sizeof(int) * (4 * (size_t)G + 1);
+  const size_t lds = kLdsG + sizeof(int) * (3 * (size_t)G + 1);
   const long long items = (long long)G * (K / BMK) * (N / BNN);
   const dim3 grid((unsigned)std::min<long long>(items, device_cu_count()));   // one resident block per CU
   if (grad_e5m2)
