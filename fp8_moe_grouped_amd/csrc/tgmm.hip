@@ -15,13 +15,14 @@
 //     the pair's valid rows once, reduces the column amax (wave shuffles +
 //     LDS), writes the scales and stores the 8-bit codes row-major into the
 //     pair's slab of the workspace ([512 rows][columns], rows past the pair's
-//     end up to the next multiple of 64 hold zero codes).
+//     end up to the next multiple of 32 hold zero codes).
 //  2. gemm: persistent, one block per CU, walking its share of the work
 //     items (expert, 256-row k tile, 128-column n tile); an item covers the
-//     expert's pairs 64 rows at a time.  The code chunks of both operands are
-//     copied HBM -> LDS by buffer loads with an LDS destination through a
-//     five-stage ring that runs across pairs and items, so copy latency is
-//     paid once per block rather than once per tile.  The contraction runs
+//     expert's pairs 128 rows at a time.  The code chunks of both operands
+//     are copied HBM -> LDS by buffer loads with an LDS destination through a
+//     three-stage ring that runs across pairs and items, so copy latency is
+//     paid once per block rather than once per tile; a pair's last stage
+//     reads zeros past its padded rows (the copy's buffer range ends there).  The contraction runs
 //     over rows, which is the slow axis of both tiles, so the MFMA operands
 //     are read with the transposing ds_read_tr8_b64 (8 consecutive rows of
 //     one column per lane) and widened to bf16 exactly.  bf16 MFMA (every
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(256) void dense_quant_kernel(const uint16_t* __rest
 }
 
 // The valid rows' codes of the buffer-wide operands into the GEMM's pair
-// slabs (zeros up to the 64-row chunk), with per-pair scales 1 for the lhs
+// slabs (zeros up to the next 32 rows), with per-pair scales 1 for the lhs
 // (its row scales are inside the gradient) and scol for the gradient.
 __global__ __launch_bounds__(kThreads) void dense_gather_kernel(const uint8_t* __restrict__ qLd,
                                                                 const uint8_t* __restrict__ qDd,
