@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
 # were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "957212819c7f3502", 2261, 77),
-    "wo_gemm": ("gmm_fwd.hip", "957212819c7f3502", 849, 270),
-    "wi_dlhs": ("dlhs.hip", "b62e3797d9e441f6", 2289, 269),
-    "wo_dlhs": ("dlhs.hip", "b62e3797d9e441f6", 1263, 77),
-    "tgmm": ("tgmm.hip", "ba9d449f75ad065a", 346 + 1450, 188 + 1926),
-    "dequant": ("dequant.hip", "1066860594ec257a", 455, 976),
+    "wi_gemm": ("gmm_fwd.hip", "7a910c596f23b235", 2272, 77),
+    "wo_gemm": ("gmm_fwd.hip", "7a910c596f23b235", 843, 270),
+    "wi_dlhs": ("dlhs.hip", "d6b3f39b49056cec", 2289, 269),
+    "wo_dlhs": ("dlhs.hip", "d6b3f39b49056cec", 1263, 77),
+    "tgmm": ("tgmm.hip", "b4ced23c8fa84cde", 346 + 1362, 181 + 1928),
+    "dequant": ("dequant.hip", "1066860594ec257a", 455, 978),
 }
 
 
