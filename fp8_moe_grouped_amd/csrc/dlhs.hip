@@ -29,8 +29,10 @@
 //
 // Inner loop: a wave keeps its 128-row dout operand of the stage in registers
 // and streams its weight fragments (16 output columns each): the next
-// fragment is read from LDS with its 16 scales and decoded, scaled and
-// rounded on the VALU between the 16 MFMAs of the current one; during the
+// fragment is read from LDS, decoded, scaled and rounded on the VALU between
+// the 16 MFMAs of the current one (the stage's scales are read once, one per
+// lane, and a DPP row broadcast inside each multiply hands every lane the
+// scale of its contraction index); during the
 // last fragment the dout operand of the next stage is reread in place right
 // after the MFMAs that last use each register.  Each lane reads 16 consecutive
 // contraction values of a row, which the two 16x16x32 MFMAs of a stage take
@@ -80,19 +82,39 @@ struct Cfg {
   static_assert(kLds + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
 };
 
-// 16-byte chunk swizzles, conflict-free for the operand reads (16 lanes read
-// 16 consecutive rows at one logical chunk).
-__device__ __forceinline__ int a_swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
-__device__ __forceinline__ int w_swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// 16-byte chunk swizzles of the operand tiles.  An operand read has 16 lanes
+// on 16 consecutive rows at one logical chunk (the four 16-lane rows of a
+// wave at four chunks).  The XOR keys were chosen by measurement on gfx950
+// (LDS bank-conflict cycles per ds_read_b128 over every linear key of the
+// row's low four bits): these take 4 LDS cycles per read; the plain
+// (row >> 1) / (row >> 2) keys took 8.
+//   128-byte rows (dout, bf16 weights): chunk ^= row bit 1 | row bit 3 << 2
+//   64-byte rows (weight codes):        chunk ^= row bit 3 << 1
+__device__ __forceinline__ int a_key(int row) { return ((row >> 1) & 1) | (((row >> 3) & 1) << 2); }
+__device__ __forceinline__ int w_key(int row) { return ((row >> 3) & 1) << 1; }
+__device__ __forceinline__ int a_swz(int row, int chunk) { return row * 128 + ((chunk ^ a_key(row)) << 4); }
+__device__ __forceinline__ int w_swz(int row, int chunk) { return row * 64 + ((chunk ^ w_key(row)) << 4); }
 
 __device__ __forceinline__ v8bf as_bf(const v4i& v) { return __builtin_bit_cast(v8bf, v); }
 
-// 8 codes (two dwords, n = 0..7 of sc) -> 8 bf16 weights.
-__device__ __forceinline__ v4i deq8(uint32_t w0, uint32_t w1, const float* sc) {
+// The value that lane I of this lane's 16-lane row holds (DPP row_newbcast;
+// the compiler folds it into the multiply that consumes it).
+template <int I>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + I, 0xf, 0xf, false));
+}
+
+// 8 codes (two dwords) -> 8 bf16 weights.  Lane i of a 16-lane row holds the
+// scale of contraction index i of the row's 16; the codes are indices
+// 8H .. 8H+7.
+template <int H>
+__device__ __forceinline__ v4i deq8(uint32_t w0, uint32_t w1, float srow) {
   const v2f a = dec_e4m3x2<false>(w0), b = dec_e4m3x2<true>(w0);
   const v2f c = dec_e4m3x2<false>(w1), d = dec_e4m3x2<true>(w1);
-  return (v4i){(int)pack_bf16x2(a[0] * sc[0], a[1] * sc[1]), (int)pack_bf16x2(b[0] * sc[2], b[1] * sc[3]),
-               (int)pack_bf16x2(c[0] * sc[4], c[1] * sc[5]), (int)pack_bf16x2(d[0] * sc[6], d[1] * sc[7])};
+  return (v4i){(int)pack_bf16x2(a[0] * row_bcast<8 * H + 0>(srow), a[1] * row_bcast<8 * H + 1>(srow)),
+               (int)pack_bf16x2(b[0] * row_bcast<8 * H + 2>(srow), b[1] * row_bcast<8 * H + 3>(srow)),
+               (int)pack_bf16x2(c[0] * row_bcast<8 * H + 4>(srow), c[1] * row_bcast<8 * H + 5>(srow)),
+               (int)pack_bf16x2(d[0] * row_bcast<8 * H + 6>(srow), d[1] * row_bcast<8 * H + 7>(srow))};
 }
 
 __device__ __forceinline__ float bf16_lo(int v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
@@ -153,7 +175,7 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
 #pragma unroll
   for (int j = 0; j < C::kALoads; ++j) {
     const int r = (C::kALoads * wave + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int c = (lane & 7) ^ a_key(r);
     va[j] = (uint32_t)min(r, rows - 1) * (uint32_t)N * 2u + (uint32_t)(c << 4);
   }
   uint32_t vw[C::kWLoads];
@@ -161,11 +183,11 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   for (int j = 0; j < C::kWLoads; ++j) {
     if (FROM_CODES) {
       const int kr = (C::kWLoads * wave + j) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((kr >> 2) & 3);
+      const int c = (lane & 3) ^ w_key(kr);
       vw[j] = (uint32_t)(nt * BN + kr) * (uint32_t)N + (uint32_t)(c << 4);
     } else {
       const int kr = (C::kWLoads * wave + j) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((kr >> 1) & 7);
+      const int c = (lane & 7) ^ a_key(kr);
       vw[j] = (uint32_t)(nt * BN + kr) * (uint32_t)N * 2u + (uint32_t)(c << 4);
     }
   }
@@ -180,7 +202,11 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   for (int s = 0; s < 2; ++s)
     w_rd[s] = C::kABytes + (FROM_CODES ? w_swz(wn * (16 * NJ) + (lane & 15), q)           // + j * 1024
                                        : a_swz(wn * (16 * NJ) + (lane & 15), 2 * q + s));  // + j * 2048
-  const int s_rd = C::kABytes + C::kWBytes + q * 64;
+  // Lane l reads scale l of the stage: the 16 lanes of row q then hold the
+  // scales of contraction indices 16q .. 16q+15, the ones the row's weight
+  // values need (one conflict-free read per stage instead of each lane
+  // reading the row's 16 scales from the same addresses).
+  const int s_rd = C::kABytes + C::kWBytes + 4 * lane;
 
   // copy number c (0 .. kLoads-1) of stage ks into slot St
   auto issue_one = [&](uint8_t* St, int ks, int c) {
@@ -206,17 +232,17 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     }
     return r;
   };
+  auto read_s = [&](const uint8_t* St) {
+    return FROM_CODES ? *reinterpret_cast<const float*>(St + s_rd) : 0.f;
+  };
   // raw fragment -> the two MFMA operands (halves n = 0..7 and 8..15 of the lane's 16)
-  auto convert = [&](const uint8_t* St, const v8i& r, v4i* w) {
+  auto convert = [&](float srow, const v8i& r, v4i* w) {
     if (FROM_CODES) {
-      float sc[16];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v4f v = *reinterpret_cast<const v4f*>(St + s_rd + 16 * t);
-        sc[4 * t] = v[0]; sc[4 * t + 1] = v[1]; sc[4 * t + 2] = v[2]; sc[4 * t + 3] = v[3];
-      }
-      w[0] = deq8((uint32_t)r[0], (uint32_t)r[1], sc);
-      w[1] = deq8((uint32_t)r[2], (uint32_t)r[3], sc + 8);
+      // opaque copy: the broadcasts stay inside this fragment's multiplies
+      // instead of being hoisted into 16 extra moves shared by the fragments
+      asm volatile("" : "+v"(srow));
+      w[0] = deq8<0>((uint32_t)r[0], (uint32_t)r[1], srow);
+      w[1] = deq8<1>((uint32_t)r[2], (uint32_t)r[3], srow);
     } else {
       w[0] = (v4i){r[0], r[1], r[2], r[3]};
       w[1] = (v4i){r[4], r[5], r[6], r[7]};
@@ -249,7 +275,8 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
 #pragma unroll
     for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(slot(0) + a_rd[s] + f * 2048);
   v4i wcur[2];
-  convert(slot(0), read_w(slot(0), 0), wcur);
+  float scur = read_s(slot(0));
+  convert(scur, read_w(slot(0), 0), wcur);
 
   static_assert(S == 3, "the copy slot must differ from the two slots read in a stage");
   // One stage.  ISSUE: copy stage ks+2 into `wr` (the slot of stage ks-1,
@@ -277,9 +304,9 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
         barrier_only();
       }
       v8i raw;
-      const uint8_t* rs_slot = rd;
+      float snext = scur;
       if (j + 1 < NJ) raw = read_w(rd, j + 1);
-      else if (MORE) { raw = read_w(rn, 0); rs_slot = rn; }
+      else if (MORE) { raw = read_w(rn, 0); snext = read_s(rn); }
       sched_fence();
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -290,10 +317,11 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
           if (MORE && j == NJ - 1) a[f][s] = *reinterpret_cast<const v4i*>(rn + a_rd[s] + f * 2048);
         }
       v4i wnext[2];
-      if (j + 1 < NJ || MORE) convert(rs_slot, raw, wnext);
+      if (j + 1 < NJ || MORE) convert(snext, raw, wnext);
       sched_fence();
       wcur[0] = wnext[0];
       wcur[1] = wnext[1];
+      scur = snext;
     }
   };
   using T_ = std::true_type;
