@@ -263,13 +263,20 @@ __device__ __forceinline__ int find_group(const int* tpre, int G, int mt) {
   return lo;
 }
 
-// Bijection of block ids [0, total) so that each of the 8 XCDs (blocks are
-// dispatched round-robin over XCDs) works on a contiguous range of logical
-// tiles and shares their operands in its own L2.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-  const int q = total / 8;
-  if (b >= 8 * q) return b;
-  return (b % 8) * q + b / 8;
+// Logical tile of block b in the m-grouped raster of the GEMMs: groups of
+// kGroupM m-tiles walk the n-tiles, m fastest.  Blocks are dispatched
+// round-robin over the 8 XCDs, so with kGroupM = 8 each XCD takes one m-tile
+// of a group through all its n-tiles and keeps that tile's rows in its own
+// L2 (the weights come from the MALL).  Measured on the bench GEMMs, this
+// beat a remap that gives each XCD a contiguous range of logical tiles by
+// 2-6 %.
+template <int kGroupM>
+__device__ __forceinline__ void raster_tile(int b, int T, int n_tiles, int& mt, int& nt) {
+  const int width = kGroupM * n_tiles;
+  const int first_m = (b / width) * kGroupM;
+  const int gsz = min(T - first_m, kGroupM);
+  mt = first_m + (b % width) % gsz;
+  nt = (b % width) / gsz;
 }
 
 }  // namespace fp8gmm

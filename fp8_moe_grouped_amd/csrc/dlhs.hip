@@ -155,13 +155,11 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   const int b = blockIdx.x;
   if (b >= total) return;
 
-  const int L = xcd_remap(b, total);
-  const int width = kGroupM * n_tiles;
-  const int first_m = (L / width) * kGroupM;
-  const int gsz = min(T - first_m, kGroupM);
-  const int mt = first_m + (L % width) % gsz;
+  // ---- tile selection: groups of kGroupM m-tiles walk the n-tiles
+  int mt, nt;
+  raster_tile<kGroupM>(b, T, n_tiles, mt, nt);
   // values read from the LDS table are wave-uniform: keep them in scalar registers
-  const int nt = __builtin_amdgcn_readfirstlane((L % width) / gsz);
+  nt = __builtin_amdgcn_readfirstlane(nt);
   const int g = __builtin_amdgcn_readfirstlane(find_group(t_pre, G, mt));
   const int row0 = __builtin_amdgcn_readfirstlane(t_start[g] + (mt - t_pre[g]) * BM);
   const int rows = __builtin_amdgcn_readfirstlane(min(BM, t_end[g] - row0));

@@ -31,8 +31,8 @@
 // epilogue scales, optionally applies SwiGLU, and stores 8-byte bf16 groups.
 //
 // Scheduling: every block rebuilds the expert table from group_sizes (a wave
-// scan), maps its id to a (global m-tile, n-tile) pair with an XCD-aware,
-// m-grouped order, and exits if it has no tile.  Tiles are aligned to each
+// scan), maps its id to a (global m-tile, n-tile) pair in an m-grouped order
+// (one m-tile of each group per XCD), and exits if it has no tile.  Tiles are aligned to each
 // expert's first row; rows past an expert's end are never read (the load row
 // is clamped inside the expert) and never written.
 #include "common.hpp"
@@ -130,14 +130,11 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   const int b = blockIdx.x;
   if (b >= total) return;
 
-  // ---- tile selection: XCD-aware, groups of kGroupM m-tiles walk the n-tiles
-  const int L = xcd_remap(b, total);
-  const int width = kGroupM * n_tiles;
-  const int first_m = (L / width) * kGroupM;
-  const int gsz = min(T - first_m, kGroupM);
-  const int mt = first_m + (L % width) % gsz;
+  // ---- tile selection: groups of kGroupM m-tiles walk the n-tiles
+  int mt, nt;
+  raster_tile<kGroupM>(b, T, n_tiles, mt, nt);
   // values read from the LDS table are wave-uniform: keep them in scalar registers
-  const int nt = __builtin_amdgcn_readfirstlane((L % width) / gsz);
+  nt = __builtin_amdgcn_readfirstlane(nt);
   const int g = __builtin_amdgcn_readfirstlane(find_group(t_pre, G, mt));
   const int row0 = __builtin_amdgcn_readfirstlane(t_start[g] + (mt - t_pre[g]) * BM);
   const int rows = __builtin_amdgcn_readfirstlane(min(BM, t_end[g] - row0));
