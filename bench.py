@@ -189,6 +189,50 @@ def tgmm_dense_vs_in_kernel(G, stream, lhs, dout, gs, mv):
             "in_kernel_ms": round(t_i, 4), "dense_ms": round(t_d, 4), "dense_over_in_kernel": round(t_d / t_i, 3)}
 
 
+def vendor_dense(stream, mv, wi_gemm_ms, wi_dlhs_ms):
+    """Reference point for the GEMM rates: the vendor library (hipBLASLt,
+    through torch) on one dense matrix with the same flops as the grouped
+    GEMMs' valid rows (no experts, no ragged tails, no scales): the FP8
+    forward shape (mv x 7168 by 7168 x 4096, e4m3, f32 accumulation, bf16
+    out) and the bf16 dLHS shape (mv x 4096 by 4096 x 7168).  Random values;
+    only the time is used.  Not part of the library's path."""
+    import torch
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(n):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / n
+
+    out = {"workload": f"one dense matrix of {mv} rows: FP8 {mv}x7168 @ 7168x4096 and bf16 {mv}x4096 @ 4096x7168"}
+    fl = 2.0 * mv * 7168 * 4096
+    g = torch.Generator(device="cuda").manual_seed(5)
+    try:
+        a8 = torch.randn(mv, 7168, device="cuda", generator=g).to(torch.float8_e4m3fn)
+        b8 = torch.randn(4096, 7168, device="cuda", generator=g).to(torch.float8_e4m3fn).t()   # column-major
+        one = torch.ones((), device="cuda")
+        t = timed(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+        out["fp8_ms"] = round(t, 4)
+        out["fp8_tflops"] = round(fl / t / 1e9, 1)
+        out["wi_gemm_rate_over_vendor"] = round(t / wi_gemm_ms, 3)
+        del a8, b8
+    except Exception as e:   # FP8 GEMM not offered by this torch build
+        out["fp8_error"] = str(e)[:200]
+    a = torch.randn(mv, 4096, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(4096, 7168, device="cuda", generator=g).to(torch.bfloat16)
+    t = timed(lambda: torch.mm(a, b))
+    out["bf16_ms"] = round(t, 4)
+    out["bf16_tflops"] = round(fl / t / 1e9, 1)
+    out["wi_dlhs_rate_over_vendor"] = round(t / wi_dlhs_ms, 3)
+    return out
+
+
 def lhs_quant_variants(G, stream, x, codes, scale, gs, mv):
     """The forward's ops-level LHS-quantization variants on the dropless wi
     input (K = 7168, N = 4096 without SwiGLU): quantizer + GEMM per call."""
@@ -364,6 +408,7 @@ def main():
     ap.add_argument("--no-micro", action="store_true", help="skip the pages' microbenchmark shape")
     ap.add_argument("--no-variants", action="store_true", help="skip the LHS-quantization variants")
     ap.add_argument("--no-dense", action="store_true", help="skip the buffer-wide tgmm baseline")
+    ap.add_argument("--no-vendor", action="store_true", help="skip the vendor dense-GEMM reference")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy (read MIB, write MIB) three times; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE hardware counters to bytes")
@@ -521,6 +566,7 @@ def main():
     variants = None if args.no_variants else lhs_quant_variants(G, stream, lhs_wi, codes_wi, scale_wi, gs, mv)
     dense = None if args.no_dense else tgmm_dense_vs_in_kernel(G, stream, lhs_t, dout_t, gs, mv)
     micro = None if args.no_micro else pages_microbench(G, stream)
+    vendor = None if args.no_vendor else vendor_dense(stream, mv, kern["wi_gemm"]["ms"], ops["wi_dlhs"]["ms"])
     ffn = None if args.no_ffn else ffn_step(G, args, gs, lhs_wi, codes_wi, scale_wi, codes_wo, scale_wo, dout_wo,
                                             int(np.sum(d["gs"])), stream)
 
@@ -558,6 +604,7 @@ def main():
         "pages_microbench": micro,
         "lhs_quant_variants": variants,
         "tgmm_dense_baseline": dense,
+        "vendor_dense": vendor,
     }
     print(json.dumps(line), flush=True)
 
