@@ -49,11 +49,13 @@ constexpr int kStages = 4;
 constexpr int kThreads = 512;       // 8 waves, two per SIMD
 constexpr int kGroupM = 8;
 
+constexpr int kScaleBytes = 2048;   // the tile's 256 column scales, then its 256 row scales
 template <int BN>
 constexpr int stage_bytes() { return BM * BK + BK * BN; }
 template <int BN>
-constexpr int lds_main() { return kStages * stage_bytes<BN>(); }
-static_assert(lds_main<256>() + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
+constexpr int lds_main() { return kStages * stage_bytes<BN>() + kScaleBytes; }
+static_assert(lds_main<256>() + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024,
+              "ring + tile scales + expert table fit the LDS");
 
 // 16-byte chunk swizzles: 16 lanes reading 16 consecutive activation rows at
 // one chunk, and two transposing-read groups (8 weight rows each, adjacent
@@ -267,6 +269,26 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
     if (kBlockQ && ((k & 7) == 7 || k + 1 == nk)) fold(k >> 3);
   };
 
+  // ---- the tile's scales go to LDS ahead of stage 0 (they are older than
+  // stage 0's copies, so they have landed whenever it has): wave 0 copies the
+  // 256 column scales (SwiGLU: the 128 gate, then the 128 up columns), wave 1
+  // the 256 row scales (rows past the tile's end read as zero).  The epilogue
+  // then reads no global memory.
+  constexpr bool kLdsScales = !BF16 && VAR == 0;
+  uint8_t* const sc_lds = smem + kStages * kStageBytes;
+  if (kLdsScales && wave == 0) {
+    const int l = (BN == 256) ? lane : (lane & 31);
+    int col;
+    if (SWIGLU) col = (l < 32) ? nt * (BN / 2) + 4 * l : I + nt * (BN / 2) + 4 * (l - 32);
+    else col = nt * BN + 4 * l;
+    dma16(make_rsrc(wscale + (size_t)g * N, (uint32_t)N * 4u), sc_lds, (uint32_t)col * 4u, 0);
+  } else if (kLdsScales && wave == 1) {
+    // one dword per lane and copy, so each row is range-checked on its own
+    const BufRsrc rr = make_rsrc(ascale + row0, (uint32_t)rows * 4u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma4(rr, sc_lds + 1024 + 256 * t, (uint32_t)lane * 4u, (uint32_t)t * 256u);
+  }
+
   // ---- prologue: stages 0..3 in flight, stage 0 landed and in registers
   const int pre = min(nk, kStages);
   for (int s = 0; s < pre; ++s)
@@ -342,21 +364,39 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   const float* ws = BF16 ? nullptr : wscale + (size_t)g * N;
   const v4f ones = {1.f, 1.f, 1.f, 1.f};
   const int hl = 4 * (lane >> 5);
+  // Lanes l and l+32 hold the same row: pq[q] holds columns 8q+0..3 (lane l)
+  // or 8q+4..7 (lane l+32) of a 32-column fragment.  Trading two 8-byte groups
+  // gives lane l columns 0-7 and 16-23 and lane l+32 columns 8-15 and 24-31, so
+  // every store is 16 bytes and each store instruction writes 32 contiguous
+  // bytes of every row it touches (with 8-byte stores the epilogue cost a
+  // fifth of the short-K forward's time).
+  auto store_frag = [&](uint16_t* rowp, const v2i* pq) __attribute__((always_inline)) {
+    const bool lo = (lane & 32) == 0;
+    const v2i s0 = lo ? pq[1] : pq[0], s1 = lo ? pq[3] : pq[2];
+    const int r00 = __shfl_xor(s0[0], 32), r01 = __shfl_xor(s0[1], 32);
+    const int r10 = __shfl_xor(s1[0], 32), r11 = __shfl_xor(s1[1], 32);
+    const v4i x0 = lo ? (v4i){pq[0][0], pq[0][1], r00, r01} : (v4i){r00, r01, pq[1][0], pq[1][1]};
+    const v4i x1 = lo ? (v4i){pq[2][0], pq[2][1], r10, r11} : (v4i){r10, r11, pq[3][0], pq[3][1]};
+    *reinterpret_cast<v4i*>(rowp + (lo ? 0 : 8)) = x0;
+    *reinterpret_cast<v4i*>(rowp + (lo ? 16 : 24)) = x1;
+  };
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int ml = wm * 64 + i * 32 + (lane & 31);
     if (ml < rows) {
       const int row = row0 + ml;
-      const float sr = (BF16 || kBlockQ) ? 1.f : ascale[row];
+      const float sr = (BF16 || kBlockQ) ? 1.f
+                       : (kLdsScales ? reinterpret_cast<const float*>(sc_lds + 1024)[ml] : ascale[row]);
       if (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           v2i pgq[4], puq[4];   // pre-activation of columns 8q + hl + 0..3, gate and up
+          v2i poq[4];           // output of the same columns
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = nt * (BN / 2) + wn * 64 + 32 * j + 8 * q + hl;
-            const v4f sg = BF16 ? ones : *reinterpret_cast<const v4f*>(ws + c);
-            const v4f su = BF16 ? ones : *reinterpret_cast<const v4f*>(ws + I + c);
+            const v4f sg = BF16 ? ones : *reinterpret_cast<const v4f*>(sc_lds + 4 * (c - nt * (BN / 2)));
+            const v4f su = BF16 ? ones : *reinterpret_cast<const v4f*>(sc_lds + 512 + 4 * (c - nt * (BN / 2)));
             float o[4], yg[4], yu[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -364,15 +404,14 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
               yu[e] = (acc[i][j + 2][4 * q + e] * sr) * su[e];
               o[e] = yg[e] / (1.0f + __expf(-yg[e])) * yu[e];
             }
-            v2i pk;
-            pk[0] = (int)pack_bf16x2(o[0], o[1]);
-            pk[1] = (int)pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<v2i*>(out + (size_t)row * I + c) = pk;
+            poq[q][0] = (int)pack_bf16x2(o[0], o[1]);
+            poq[q][1] = (int)pack_bf16x2(o[2], o[3]);
             pgq[q][0] = (int)pack_bf16x2(yg[0], yg[1]);
             pgq[q][1] = (int)pack_bf16x2(yg[2], yg[3]);
             puq[q][0] = (int)pack_bf16x2(yu[0], yu[1]);
             puq[q][1] = (int)pack_bf16x2(yu[2], yu[3]);
           }
+          store_frag(out + (size_t)row * I + nt * (BN / 2) + wn * 64 + 32 * j, poq);
           if (preact) {
             // Lanes l and l+32 hold the same row, columns 8q+0..3 and 8q+4..7.  Trading one
             // 8-byte half per column pair makes each lane own 8 consecutive columns, so the
@@ -397,21 +436,24 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < NJ; ++j) {
+          v2i pq[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = nt * BN + wn * (BN / 2) + 32 * j + 8 * q + hl;
-            const v4f sc = BF16 ? ones : *reinterpret_cast<const v4f*>(ws + c);
+            const v4f sc = BF16 ? ones
+                           : (kLdsScales ? *reinterpret_cast<const v4f*>(sc_lds + 4 * (c - nt * BN))
+                                         : *reinterpret_cast<const v4f*>(ws + c));
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               v[e] = kBlockQ ? tot[i][j][4 * q + e]
                              : (kRhsFirst ? (acc[i][j][4 * q + e] * sc[e]) * sr : (acc[i][j][4 * q + e] * sr) * sc[e]);
-            v2i pk;
-            pk[0] = (int)pack_bf16x2(v[0], v[1]);
-            pk[1] = (int)pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<v2i*>(out + (size_t)row * N + c) = pk;
+            pq[q][0] = (int)pack_bf16x2(v[0], v[1]);
+            pq[q][1] = (int)pack_bf16x2(v[2], v[3]);
           }
+          store_frag(out + (size_t)row * N + nt * BN + wn * (BN / 2) + 32 * j, pq);
+        }
       }
     }
   }
