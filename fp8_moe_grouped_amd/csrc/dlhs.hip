@@ -330,6 +330,19 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   step(ks, F_{}, F_{}, slot(ks + 2), slot(ks), slot(ks + 1));
 
   // ---- epilogue: lane owns row wm*128 + f*16 + lane%16, columns wn*BN/4 + j*16 + 4*(lane/16) + 0..3
+  // Lanes l and l^16 hold the same row, columns 4q..4q+3 and 4q+4..4q+7 (q even)
+  // of two adjacent 16-column fragments.  Trading one 8-byte group gives the
+  // even-q lane 8 columns of the first fragment and the odd-q lane 8 of the
+  // second, so every store is 16 bytes and an instruction writes 64 contiguous
+  // bytes of each row (p: the row at the first fragment's column 0).
+  static_assert(NJ % 2 == 0, "fragments are stored in pairs");
+  auto store_pair = [&](uint16_t* p, const v2i& x0, const v2i& x1) __attribute__((always_inline)) {
+    const bool ev = (q & 1) == 0;
+    const v2i sv = ev ? x1 : x0;
+    const int r0 = __shfl_xor(sv[0], 16), r1 = __shfl_xor(sv[1], 16);
+    const v4i v = ev ? (v4i){x0[0], x0[1], r0, r1} : (v4i){r0, r1, x1[0], x1[1]};
+    *reinterpret_cast<v4i*>(p + (ev ? 4 * q : 16 + 4 * (q - 1))) = v;
+  };
   if (DSWIGLU) {
     // output and pre-activation rows are [gate | up], 2K wide
     const size_t ld = 2 * (size_t)K;
@@ -337,13 +350,15 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     for (int f = 0; f < 8; ++f) {
       const int ml = wm * 128 + f * 16 + (lane & 15);
       if (ml < rows) {
-        const size_t rb = (size_t)(row0 + ml) * ld + nt * BN + wn * (16 * NJ) + 4 * q;
+        const size_t rb0 = (size_t)(row0 + ml) * ld + nt * BN + wn * (16 * NJ);
+        const size_t rb = rb0 + 4 * q;
         v2i gb[NJ], ub[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           gb[j] = *reinterpret_cast<const v2i*>(preact + rb + j * 16);
           ub[j] = *reinterpret_cast<const v2i*>(preact + rb + K + j * 16);
         }
+        v2i pg[NJ], pu[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           float dg[4], du[4];
@@ -351,13 +366,15 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
           dswiglu1(acc[f][j][1], bf16_hi(gb[j][0]), bf16_hi(ub[j][0]), dg[1], du[1]);
           dswiglu1(acc[f][j][2], bf16_lo(gb[j][1]), bf16_lo(ub[j][1]), dg[2], du[2]);
           dswiglu1(acc[f][j][3], bf16_hi(gb[j][1]), bf16_hi(ub[j][1]), dg[3], du[3]);
-          v2i pg, pu;
-          pg[0] = (int)pack_bf16x2(dg[0], dg[1]);
-          pg[1] = (int)pack_bf16x2(dg[2], dg[3]);
-          pu[0] = (int)pack_bf16x2(du[0], du[1]);
-          pu[1] = (int)pack_bf16x2(du[2], du[3]);
-          *reinterpret_cast<v2i*>(dlhs + rb + j * 16) = pg;
-          *reinterpret_cast<v2i*>(dlhs + rb + K + j * 16) = pu;
+          pg[j][0] = (int)pack_bf16x2(dg[0], dg[1]);
+          pg[j][1] = (int)pack_bf16x2(dg[2], dg[3]);
+          pu[j][0] = (int)pack_bf16x2(du[0], du[1]);
+          pu[j][1] = (int)pack_bf16x2(du[2], du[3]);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; j += 2) {
+          store_pair(dlhs + rb0 + j * 16, pg[j], pg[j + 1]);
+          store_pair(dlhs + rb0 + K + j * 16, pu[j], pu[j + 1]);
         }
       }
     }
@@ -367,14 +384,15 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   for (int f = 0; f < 8; ++f) {
     const int ml = wm * 128 + f * 16 + (lane & 15);
     if (ml < rows) {
-      uint16_t* orow = dlhs + (size_t)(row0 + ml) * K + nt * BN + wn * (16 * NJ) + 4 * q;
+      uint16_t* orow = dlhs + (size_t)(row0 + ml) * K + nt * BN + wn * (16 * NJ);
+      v2i pk[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        v2i pk;
-        pk[0] = (int)pack_bf16x2(acc[f][j][0], acc[f][j][1]);
-        pk[1] = (int)pack_bf16x2(acc[f][j][2], acc[f][j][3]);
-        *reinterpret_cast<v2i*>(orow + j * 16) = pk;
+        pk[j][0] = (int)pack_bf16x2(acc[f][j][0], acc[f][j][1]);
+        pk[j][1] = (int)pack_bf16x2(acc[f][j][2], acc[f][j][3]);
       }
+#pragma unroll
+      for (int j = 0; j < NJ; j += 2) store_pair(orow + j * 16, pk[j], pk[j + 1]);
     }
   }
 }
