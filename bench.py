@@ -233,6 +233,63 @@ def vendor_dense(stream, mv, wi_gemm_ms, wi_dlhs_ms):
     return out
 
 
+def skinny_groups(G, stream, codes_wi, scale_wi, codes_wo, scale_wo, rows_per_expert=16):
+    """Skinny groups: every one of the 32 experts gets only a few rows
+    (16 = 64 tokens x top-8 / 32, a decode-like batch), so the forward and
+    the dLHS are bound by reading each expert's weight codes once.  Reported
+    as HBM GB/s of the algorithmic bytes: codes + scales of every expert,
+    bf16 activations read, bf16 output written (the quantizer pass of the
+    forward is timed with it)."""
+    import torch
+    Gn, K1, N1 = codes_wi.shape
+    _, K2, N2 = codes_wo.shape
+    M = Gn * rows_per_expert
+    gs = torch.full((Gn,), rows_per_expert, dtype=torch.int32, device=codes_wi.device)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x1 = torch.randn(M, K1, device="cuda", generator=g).to(torch.bfloat16)
+    x2 = torch.randn(M, K2, device="cuda", generator=g).to(torch.bfloat16)
+    d1 = (torch.randn(M, N1, device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
+    d2 = (torch.randn(M, N2, device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
+    h = torch.empty(M, N1 // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(M, N2, dtype=torch.bfloat16, device="cuda")
+    dx1 = torch.empty(M, K1, dtype=torch.bfloat16, device="cuda")
+    dx2 = torch.empty(M, K2, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(n):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / n
+
+    def gbs(nbytes, ms):
+        return round(nbytes / ms / 1e6, 1)
+
+    w1 = Gn * K1 * N1 + Gn * N1 * 4
+    w2 = Gn * K2 * N2 + Gn * N2 * 4
+    out = {"workload": f"{Gn} experts x {rows_per_expert} rows ({M} rows): wi {K1} -> 2x{N1 // 2} SwiGLU, "
+                       f"wo {K2} -> {N2}, and their dLHS; bytes = weight codes + scales + activations + outputs",
+           "hbm_peak_gbs": HBM_PEAK_GBS}
+    ws1 = torch.empty(G.workspace_bytes(G.OP_SILU, M, K1, N1, Gn), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(G.workspace_bytes(G.OP_FWD, M, K2, N2, Gn), dtype=torch.uint8, device="cuda")
+    t = timed(lambda: G.gmm_silu_fp8(x1, codes_wi, scale_wi, gs, out=h, workspace=ws1))
+    out["wi_fwd"] = {"ms": round(t, 4), "gbs": gbs(w1 + M * K1 * 2 + M * (N1 // 2) * 2, t)}
+    t = timed(lambda: G.gmm_fp8_fwd(x2, codes_wo, scale_wo, gs, out=y, workspace=ws2))
+    out["wo_fwd"] = {"ms": round(t, 4), "gbs": gbs(w2 + M * K2 * 2 + M * N2 * 2, t)}
+    t = timed(lambda: G.gmm_dlhs_fp8(d1, codes_wi, scale_wi, gs, out=dx1))
+    out["wi_dlhs"] = {"ms": round(t, 4), "gbs": gbs(w1 + M * N1 * 2 + M * K1 * 2, t)}
+    t = timed(lambda: G.gmm_dlhs_fp8(d2, codes_wo, scale_wo, gs, out=dx2))
+    out["wo_dlhs"] = {"ms": round(t, 4), "gbs": gbs(w2 + M * N2 * 2 + M * K2 * 2, t)}
+    for k in ("wi_fwd", "wo_fwd", "wi_dlhs", "wo_dlhs"):
+        out[k]["frac_hbm"] = round(out[k]["gbs"] / HBM_PEAK_GBS, 3)
+    return out
+
+
 def lhs_quant_variants(G, stream, x, codes, scale, gs, mv):
     """The forward's ops-level LHS-quantization variants on the dropless wi
     input (K = 7168, N = 4096 without SwiGLU): quantizer + GEMM per call."""
@@ -409,6 +466,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the LHS-quantization variants")
     ap.add_argument("--no-dense", action="store_true", help="skip the buffer-wide tgmm baseline")
     ap.add_argument("--no-vendor", action="store_true", help="skip the vendor dense-GEMM reference")
+    ap.add_argument("--no-skinny", action="store_true", help="skip the skinny-groups (decode-like) measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy (read MIB, write MIB) three times; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE hardware counters to bytes")
@@ -567,6 +625,7 @@ def main():
     dense = None if args.no_dense else tgmm_dense_vs_in_kernel(G, stream, lhs_t, dout_t, gs, mv)
     micro = None if args.no_micro else pages_microbench(G, stream)
     vendor = None if args.no_vendor else vendor_dense(stream, mv, kern["wi_gemm"]["ms"], ops["wi_dlhs"]["ms"])
+    skinny = None if args.no_skinny else skinny_groups(G, stream, codes_wi, scale_wi, codes_wo, scale_wo)
     ffn = None if args.no_ffn else ffn_step(G, args, gs, lhs_wi, codes_wi, scale_wi, codes_wo, scale_wo, dout_wo,
                                             int(np.sum(d["gs"])), stream)
 
@@ -605,6 +664,7 @@ def main():
         "lhs_quant_variants": variants,
         "tgmm_dense_baseline": dense,
         "vendor_dense": vendor,
+        "skinny_groups": skinny,
     }
     print(json.dumps(line), flush=True)
 
