@@ -13,13 +13,15 @@
 // scale and rounded to bf16 (the arithmetic of dequantize_fp8_codes) before
 // it enters a bf16 MFMA with f32 accumulation.
 //
-// Tiling (gfx950): a block owns 256 rows x BN output columns of one expert
-// (BN = 256, or 128 when K is not a multiple of 256).  Eight waves, two per
-// SIMD, in a 2 x 4 grid own 128 rows x BN/4 columns each (128 f32
-// accumulators per lane); the second wave on a SIMD issues MFMAs while the
-// first waits or converts.  The contraction advances 64 per stage through a
+// Tiling (gfx950): a block owns BM rows x BN output columns of one expert
+// (BM = 256, or 64 when the buffer holds at most 64 rows per expert on
+// average, where most rows of a 256-row tile would be padding; BN = 256, or
+// 128 when K is not a multiple of 256).  Eight waves, two per SIMD, in a
+// 2 x 4 grid own BM/2 rows x BN/4 columns each (up to 128 f32 accumulators
+// per lane); the second wave on a SIMD issues MFMAs while the first waits or
+// converts.  The contraction advances 64 per stage through a
 // three-stage LDS ring (bf16 weights always use BN = 128 to fit), each holding
-//   * the dout tile, [256 rows][64 bf16], 16-byte chunks XOR-swizzled;
+//   * the dout tile, [BM rows][64 bf16], 16-byte chunks XOR-swizzled;
 //   * the weight tile in its natural [k][n] layout (n contiguous, which is the
 //     contraction), [BN rows][64 codes] or [BN rows][64 bf16], swizzled;
 //   * the 64 scales of the stage (each wave copies eight of them).
@@ -27,7 +29,7 @@
 // at the top of a stage for two stages ahead; one barrier per stage, just
 // before the next stage is first read.
 //
-// Inner loop: a wave keeps its 128-row dout operand of the stage in registers
+// Inner loop: a wave keeps its BM/2-row dout operand of the stage in registers
 // and streams its weight fragments (16 output columns each): the next
 // fragment is read from LDS, decoded, scaled and rounded on the VALU between
 // the 16 MFMAs of the current one (the stage's scales are read once, one per
@@ -59,15 +61,18 @@
 namespace fp8gmm {
 namespace {
 
-constexpr int BM = 256;
 constexpr int BKN = 64;                 // contraction (n) per stage
 constexpr int kARow = BKN * 2;          // 128 bytes per dout tile row
 constexpr int kThreads = 512;           // 8 waves, two per SIMD
 constexpr int kGroupM = 8;
 
-template <bool FROM_CODES, int BN>
+// BM: rows per block tile, 256, or 64 for skinny groups (a buffer with at
+// most 64 rows per expert on average), where a 256-row tile would spend
+// most of its MFMAs on padding rows.
+template <bool FROM_CODES, int BN, int BM>
 struct Cfg {
   static constexpr int NJ = BN / 64;                         // 16-column fragments per wave
+  static constexpr int FBK = BM / 32;                        // 16-row fragments per wave (BM/2 rows)
   static constexpr int kWRow = FROM_CODES ? BKN : BKN * 2;   // bytes per weight tile row
   static constexpr int kABytes = BM * kARow;
   static constexpr int kWBytes = BN * kWRow;
@@ -128,15 +133,16 @@ __device__ __forceinline__ void dswiglu1(float dh, float g, float u, float& dg, 
   du = dh * (g * sig);
 }
 
-template <bool FROM_CODES, int BN, bool DSWIGLU>
+template <bool FROM_CODES, int BN, bool DSWIGLU, int BM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restrict__ codes,
                      const float* __restrict__ wscale, const uint16_t* __restrict__ wbf16,
                      const int* __restrict__ group_sizes, int G, int M, int K, int N,
                      const uint16_t* __restrict__ preact, uint16_t* __restrict__ dlhs, int* status) {
   static_assert(!DSWIGLU || FROM_CODES, "the dSwiGLU epilogue belongs to the FP8-code path");
-  using C = Cfg<FROM_CODES, BN>;
+  using C = Cfg<FROM_CODES, BN, BM>;
   constexpr int NJ = C::NJ;
+  constexpr int FBK = C::FBK;
   constexpr int S = C::kStages;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* t_start = reinterpret_cast<int*>(smem + C::kLds);
@@ -194,7 +200,7 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   const int q = lane >> 4;
   int a_rd[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) a_rd[s] = a_swz(wm * 128 + (lane & 15), 2 * q + s);   // + f * 2048
+  for (int s = 0; s < 2; ++s) a_rd[s] = a_swz(wm * (BM / 2) + (lane & 15), 2 * q + s);   // + f * 2048
   int w_rd[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -247,9 +253,9 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     }
   };
 
-  v4f acc[8][NJ];
+  v4f acc[FBK][NJ];
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int f = 0; f < FBK; ++f)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
@@ -267,9 +273,9 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     wait_vmem_lds<0>();
   }
   barrier_only();
-  v4i a[8][2];
+  v4i a[FBK][2];
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int f = 0; f < FBK; ++f)
 #pragma unroll
     for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(slot(0) + a_rd[s] + f * 2048);
   v4i wcur[2];
@@ -309,7 +315,7 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
+        for (int f = 0; f < FBK; ++f) {
           acc[f][j] = mfma_bf16_16x16x32(as_bf(wcur[s]), as_bf(a[f][s]), acc[f][j]);
           // last fragment of the stage: a[f][s] is free, refill it from stage ks+1
           if (MORE && j == NJ - 1) a[f][s] = *reinterpret_cast<const v4i*>(rn + a_rd[s] + f * 2048);
@@ -347,8 +353,8 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     // output and pre-activation rows are [gate | up], 2K wide
     const size_t ld = 2 * (size_t)K;
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int ml = wm * 128 + f * 16 + (lane & 15);
+    for (int f = 0; f < FBK; ++f) {
+      const int ml = wm * (BM / 2) + f * 16 + (lane & 15);
       if (ml < rows) {
         const size_t rb0 = (size_t)(row0 + ml) * ld + nt * BN + wn * (16 * NJ);
         const size_t rb = rb0 + 4 * q;
@@ -381,8 +387,8 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     return;
   }
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int ml = wm * 128 + f * 16 + (lane & 15);
+  for (int f = 0; f < FBK; ++f) {
+    const int ml = wm * (BM / 2) + f * 16 + (lane & 15);
     if (ml < rows) {
       uint16_t* orow = dlhs + (size_t)(row0 + ml) * K + nt * BN + wn * (16 * NJ);
       v2i pk[NJ];
@@ -397,28 +403,38 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   }
 }
 
-template <bool FROM_CODES, bool DSWIGLU>
-hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const float* scale, const uint16_t* wbf16,
-                            const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact,
-                            uint16_t* dlhs, int* status, hipStream_t stream) {
-  if (M == 0) return hipSuccess;
+template <bool FROM_CODES, bool DSWIGLU, int BM>
+hipError_t launch_dlhs_bm(const uint16_t* dout, const uint8_t* codes, const float* scale, const uint16_t* wbf16,
+                          const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact, uint16_t* dlhs,
+                          int* status, hipStream_t stream) {
   const long long max_m_tiles = (M + BM - 1) / BM + G;
   const size_t table = sizeof(int) * (3 * (size_t)G + 1);
   // bf16 weights always take 128-column tiles (a 256-column bf16 ring does not fit the LDS)
   if constexpr (FROM_CODES) {
     if (K % 256 == 0) {
-      hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 256, DSWIGLU>), dim3((unsigned)(max_m_tiles * (K / 256))),
-                         dim3(kThreads), (Cfg<FROM_CODES, 256>::kLds + table), stream, dout, codes, scale, wbf16,
+      hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 256, DSWIGLU, BM>), dim3((unsigned)(max_m_tiles * (K / 256))),
+                         dim3(kThreads), (Cfg<FROM_CODES, 256, BM>::kLds + table), stream, dout, codes, scale, wbf16,
                          group_sizes, G, M, K, N, preact, dlhs, status);
       return hipGetLastError();
     }
   }
-  {
-    hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 128, DSWIGLU>), dim3((unsigned)(max_m_tiles * (K / 128))),
-                       dim3(kThreads), (Cfg<FROM_CODES, 128>::kLds + table), stream, dout, codes, scale, wbf16,
-                       group_sizes, G, M, K, N, preact, dlhs, status);
-  }
+  hipLaunchKernelGGL((gmm_dlhs_kernel<FROM_CODES, 128, DSWIGLU, BM>), dim3((unsigned)(max_m_tiles * (K / 128))),
+                     dim3(kThreads), (Cfg<FROM_CODES, 128, BM>::kLds + table), stream, dout, codes, scale, wbf16,
+                     group_sizes, G, M, K, N, preact, dlhs, status);
   return hipGetLastError();
+}
+
+template <bool FROM_CODES, bool DSWIGLU>
+hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const float* scale, const uint16_t* wbf16,
+                            const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact,
+                            uint16_t* dlhs, int* status, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  // skinny groups (at most 64 rows per expert on average): 64-row tiles
+  if ((long long)M <= 64LL * G)
+    return launch_dlhs_bm<FROM_CODES, DSWIGLU, 64>(dout, codes, scale, wbf16, group_sizes, G, M, K, N, preact, dlhs,
+                                                  status, stream);
+  return launch_dlhs_bm<FROM_CODES, DSWIGLU, 256>(dout, codes, scale, wbf16, group_sizes, G, M, K, N, preact, dlhs,
+                                                 status, stream);
 }
 
 }  // namespace
