@@ -105,6 +105,31 @@ def test_dlhs_edges_and_stale_tail():
     assert st == 3
 
 
+@pytest.mark.parametrize("K", [2048, 1152])
+def test_dlhs_skinny_groups(K):
+    """Skinny groups (a buffer of at most 64 rows per expert on average):
+    the 64-row tiles.  Mixed sizes: empty experts, single rows, experts that
+    span two and three tiles, and a garbage tail; K = 1152 also takes the
+    128-column tiles."""
+    r = np.random.default_rng(21)
+    G_, N = 32, 1024
+    M = 64 * G_
+    sizes = r.integers(0, 24, G_)
+    sizes[[3, 17]] = 0
+    sizes[5], sizes[9], sizes[30] = 1, 130, 64
+    sizes = sizes.astype(np.int64)
+    assert sizes.sum() < M
+    codes = np.empty((G_, K, N), np.uint8)
+    scale = np.empty((G_, N), np.float32)
+    for g in range(G_):
+        codes[g], scale[g] = W.weight_codes(r.standard_normal((K, N)).astype(np.float32) * 0.02)
+    dout = W.to_bf16_bits(r.standard_normal((M, N)).astype(np.float32) * 1e-3)
+    W.fill_garbage(dout, int(sizes.sum()))
+    err, st = check_dlhs(dict(codes=codes, scale=scale, dout=dout), gs=sizes.tolist())
+    assert st == 0
+    print(f"skinny dlhs K={K}: normwise {err[0]:.2e} ratio {err[1]:.3f}")
+
+
 # ---------------------------------------------------------------- bf16 forward arm
 
 @pytest.mark.parametrize("config,N,silu", [(2, 2048, False), (0, 384, False), (1, 1536, True), (0, 256, True)])
