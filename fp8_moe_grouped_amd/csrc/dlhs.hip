@@ -273,27 +273,38 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     wait_vmem_lds<0>();
   }
   barrier_only();
+  // A wave whose BM/2 rows all lie past the tile's last valid row (an
+  // expert's short last tile) skips its operand reads, conversions and
+  // MFMAs; it still issues its share of the copies and joins every barrier.
+  // The two waves of a SIMD own the tile's two row halves, so a tile of at
+  // most BM/2 valid rows keeps one wave's work per SIMD.
+  const bool active = wm * (BM / 2) < rows;
   v4i a[FBK][2];
-#pragma unroll
-  for (int f = 0; f < FBK; ++f)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(slot(0) + a_rd[s] + f * 2048);
   v4i wcur[2];
-  float scur = read_s(slot(0));
-  convert(scur, read_w(slot(0), 0), wcur);
+  float scur = 0.f;
+  if (active) {
+#pragma unroll
+    for (int f = 0; f < FBK; ++f)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(slot(0) + a_rd[s] + f * 2048);
+    scur = read_s(slot(0));
+    convert(scur, read_w(slot(0), 0), wcur);
+  }
 
   static_assert(S == 3, "the copy slot must differ from the two slots read in a stage");
   // One stage.  ISSUE: copy stage ks+2 into `wr` (the slot of stage ks-1,
   // which no wave reads after the previous barrier); MORE: stage ks+1 (slot
   // `rn`) exists: the barrier before the last fragment makes sure it has
-  // landed, then its first weight fragment and its dout operand are read.
-  // `wr` is distinct from `rd`/`rn`; marking the slots __restrict__ tells the
-  // compiler the reads cannot depend on the copies issued here, so it adds
-  // no wait for them (the explicit wait + barrier order the ring).
-  auto step = [&](int ks, auto issue_c, auto more_c, uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd,
-                  const uint8_t* __restrict__ rn) {
+  // landed, then its first weight fragment and its dout operand are read;
+  // ACT: the wave computes (see above).  `wr` is distinct from `rd`/`rn`;
+  // marking the slots __restrict__ tells the compiler the reads cannot depend
+  // on the copies issued here, so it adds no wait for them (the explicit wait
+  // + barrier order the ring).
+  auto step = [&](int ks, auto issue_c, auto more_c, auto act_c, uint8_t* __restrict__ wr,
+                  const uint8_t* __restrict__ rd, const uint8_t* __restrict__ rn) {
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr bool MORE = decltype(more_c)::value;
+    constexpr bool ACT = decltype(act_c)::value;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (ISSUE) {
@@ -307,33 +318,39 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
         else wait_vmem_lds<0>();
         barrier_only();
       }
-      v8i raw;
-      float snext = scur;
-      if (j + 1 < NJ) raw = read_w(rd, j + 1);
-      else if (MORE) { raw = read_w(rn, 0); snext = read_s(rn); }
-      sched_fence();
+      if constexpr (ACT) {
+        v8i raw;
+        float snext = scur;
+        if (j + 1 < NJ) raw = read_w(rd, j + 1);
+        else if (MORE) { raw = read_w(rn, 0); snext = read_s(rn); }
+        sched_fence();
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int f = 0; f < FBK; ++f) {
-          acc[f][j] = mfma_bf16_16x16x32(as_bf(wcur[s]), as_bf(a[f][s]), acc[f][j]);
-          // last fragment of the stage: a[f][s] is free, refill it from stage ks+1
-          if (MORE && j == NJ - 1) a[f][s] = *reinterpret_cast<const v4i*>(rn + a_rd[s] + f * 2048);
-        }
-      v4i wnext[2];
-      if (j + 1 < NJ || MORE) convert(snext, raw, wnext);
-      sched_fence();
-      wcur[0] = wnext[0];
-      wcur[1] = wnext[1];
-      scur = snext;
+          for (int f = 0; f < FBK; ++f) {
+            acc[f][j] = mfma_bf16_16x16x32(as_bf(wcur[s]), as_bf(a[f][s]), acc[f][j]);
+            // last fragment of the stage: a[f][s] is free, refill it from stage ks+1
+            if (MORE && j == NJ - 1) a[f][s] = *reinterpret_cast<const v4i*>(rn + a_rd[s] + f * 2048);
+          }
+        v4i wnext[2];
+        if (j + 1 < NJ || MORE) convert(snext, raw, wnext);
+        sched_fence();
+        wcur[0] = wnext[0];
+        wcur[1] = wnext[1];
+        scur = snext;
+      }
     }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  int ks = 0;
-  for (; ks + S - 1 < nk; ++ks) step(ks, T_{}, T_{}, slot(ks + S - 1), slot(ks), slot(ks + 1));
-  if (ks + 1 < nk) { step(ks, F_{}, T_{}, slot(ks + 2), slot(ks), slot(ks + 1)); ++ks; }
-  step(ks, F_{}, F_{}, slot(ks + 2), slot(ks), slot(ks + 1));
+  auto run = [&](auto act_c) {
+    int ks = 0;
+    for (; ks + S - 1 < nk; ++ks) step(ks, T_{}, T_{}, act_c, slot(ks + S - 1), slot(ks), slot(ks + 1));
+    if (ks + 1 < nk) { step(ks, F_{}, T_{}, act_c, slot(ks + 2), slot(ks), slot(ks + 1)); ++ks; }
+    step(ks, F_{}, F_{}, act_c, slot(ks + 2), slot(ks), slot(ks + 1));
+  };
+  if (active) run(T_{});
+  else run(F_{});
 
   // ---- epilogue: lane owns row wm*128 + f*16 + lane%16, columns wn*BN/4 + j*16 + 4*(lane/16) + 0..3
   // Lanes l and l^16 hold the same row, columns 4q..4q+3 and 4q+4..4q+7 (q even)

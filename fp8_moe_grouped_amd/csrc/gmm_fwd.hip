@@ -299,31 +299,42 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   else if (pre == 2) wait_vmem_lds<kLoads>();
   else wait_vmem_lds<0>();
   barrier_only();
+  // A wave whose 64 rows all lie past the tile's last valid row (an expert's
+  // short last tile) skips its operand reads and MFMAs; it still issues its
+  // share of the copies and joins every barrier.  The two waves of a SIMD own
+  // rows 0-127 and 128-255 of the tile, so a tile of at most 128 valid rows
+  // keeps one wave's MFMAs per SIMD.
+  const bool active = wm * 64 < rows;
   v8i a[MI], bf[NJ];
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) a[i] = read_a(smem, i);
+    for (int i = 0; i < MI; ++i) a[i] = read_a(smem, i);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) bf[j] = read_b(smem, j);
+    for (int j = 0; j < NJ; ++j) bf[j] = read_b(smem, j);
+  }
 
   // One stage.  ISSUE: copy stage ks+4 into this stage's buffer `wr` (its
   // operands are in registers; the barrier makes sure every wave's are);
   // MORE: stage ks+1 (buffer `rd`) exists and is reread into the registers as
   // they free up; WAITN: copies issued after stage ks+1 that may still be in
-  // flight at the barrier.  `wr` and `rd` are distinct ring slots: marking them
-  // __restrict__ tells the compiler the reads cannot depend on the copies
-  // issued here, so it adds no wait for them (the wait + barrier above order
-  // the ring).
-  auto step = [&](int ks, auto issue_c, auto more_c, auto waitn_c, uint8_t* __restrict__ wr,
+  // flight at the barrier; ACT: the wave computes (see above).  `wr` and `rd`
+  // are distinct ring slots: marking them __restrict__ tells the compiler the
+  // reads cannot depend on the copies issued here, so it adds no wait for them
+  // (the wait + barrier above order the ring).
+  auto step = [&](int ks, auto issue_c, auto more_c, auto waitn_c, auto act_c, uint8_t* __restrict__ wr,
                   const uint8_t* __restrict__ rd) {
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr bool MORE = decltype(more_c)::value;
     constexpr int WAITN = decltype(waitn_c)::value;
+    constexpr bool ACT = decltype(act_c)::value;
     v8i an[MI];
     if (MORE) {
       wait_vmem_lds<WAITN * kLoads>();
       barrier_only();
+      if constexpr (ACT) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) an[i] = read_a(rd, i);
+        for (int i = 0; i < MI; ++i) an[i] = read_a(rd, i);
+      }
       sched_fence();
     }
 #pragma unroll
@@ -332,12 +343,14 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
 #pragma unroll
         for (int q = j * kLoads / NJ; q < (j + 1) * kLoads / NJ; ++q) issue_one(wr, ks + kStages, q);
       }
+      if constexpr (ACT) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) acc[i][j] = mma(bf[j], a[i], acc[i][j]);
-      if (MORE) bf[j] = read_b(rd, j);
+        for (int i = 0; i < MI; ++i) acc[i][j] = mma(bf[j], a[i], acc[i][j]);
+        if (MORE) bf[j] = read_b(rd, j);
+      }
       sched_fence();   // keep each refill between the MFMAs that surround it
     }
-    if (MORE) {
+    if (MORE && ACT) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) a[i] = an[i];
     }
@@ -348,16 +361,24 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   using W1 = std::integral_constant<int, 1>;
   using W2 = std::integral_constant<int, 2>;
   auto slot = [&](int s) { return smem + (s % kStages) * kStageBytes; };
-  int ks = 0;
-  for (; ks + kStages < nk; ++ks) {
-    step(ks, T_{}, T_{}, W2{}, slot(ks), slot(ks + 1));
-    maybe_fold(ks);
-  }
-  if (ks + 3 < nk) { step(ks, F_{}, T_{}, W2{}, slot(ks), slot(ks + 1)); maybe_fold(ks); ++ks; }
-  if (ks + 2 < nk) { step(ks, F_{}, T_{}, W1{}, slot(ks), slot(ks + 1)); maybe_fold(ks); ++ks; }
-  if (ks + 1 < nk) { step(ks, F_{}, T_{}, W0{}, slot(ks), slot(ks + 1)); maybe_fold(ks); ++ks; }
-  step(ks, F_{}, F_{}, W0{}, slot(ks), slot(ks));
-  maybe_fold(ks);
+  auto run = [&](auto act_c) {
+    constexpr bool ACT = decltype(act_c)::value;
+    auto fold_if = [&](int k) __attribute__((always_inline)) {
+      if constexpr (ACT) maybe_fold(k);
+    };
+    int ks = 0;
+    for (; ks + kStages < nk; ++ks) {
+      step(ks, T_{}, T_{}, W2{}, act_c, slot(ks), slot(ks + 1));
+      fold_if(ks);
+    }
+    if (ks + 3 < nk) { step(ks, F_{}, T_{}, W2{}, act_c, slot(ks), slot(ks + 1)); fold_if(ks); ++ks; }
+    if (ks + 2 < nk) { step(ks, F_{}, T_{}, W1{}, act_c, slot(ks), slot(ks + 1)); fold_if(ks); ++ks; }
+    if (ks + 1 < nk) { step(ks, F_{}, T_{}, W0{}, act_c, slot(ks), slot(ks + 1)); fold_if(ks); ++ks; }
+    step(ks, F_{}, F_{}, W0{}, act_c, slot(ks), slot(ks));
+    fold_if(ks);
+  };
+  if (active) run(T_{});
+  else run(F_{});
 
   // ---- epilogue: lane owns row wm*64 + i*32 + lane%32 and, per fragment j,
   // columns tc(j) + 8*q + 4*(lane/32) + 0..3 for q = 0..3
