@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
 # were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "969ab47399963b75", 2709, 77),
-    "wo_gemm": ("gmm_fwd.hip", "969ab47399963b75", 1314, 269),
-    "wi_dlhs": ("dlhs.hip", "8b7c6ea1f3d82283", 2716, 269),
-    "wo_dlhs": ("dlhs.hip", "8b7c6ea1f3d82283", 1425, 77),
-    "tgmm": ("tgmm.hip", "db778cbf6acd9be2", 346 + 1213, 181 + 1924),
-    "dequant": ("dequant.hip", "6f296d8865a77f01", 455, 979),
+    "wi_gemm": ("gmm_fwd.hip", "352ce484e45786a1", 2760, 77),
+    "wo_gemm": ("gmm_fwd.hip", "352ce484e45786a1", 1323, 269),
+    "wi_dlhs": ("dlhs.hip", "ac6a85033b161900", 2823, 269),
+    "wo_dlhs": ("dlhs.hip", "ac6a85033b161900", 1427, 77),
+    "tgmm": ("tgmm.hip", "db778cbf6acd9be2", 346 + 1181, 181 + 1925),
+    "dequant": ("dequant.hip", "6f296d8865a77f01", 455, 977),
 }
 
 

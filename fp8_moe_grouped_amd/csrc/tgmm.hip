@@ -31,9 +31,12 @@
 //     adder, about 2^-16 of the absolute sum, too coarse for an f32 gradient.
 //     Eight waves (two per SIMD) own 64 x 64 of the tile each; a per-pair
 //     partial accumulator is rescaled by sL x sD and added to the total at
-//     the pair's end.  Experts without rows get zeros.  The f32 output is
-//     written with 16-byte streaming stores, which drain while the next item
-//     computes.
+//     the pair's end.  The pair's scales travel with each stage's copy into
+//     the ring, so the rescale reads LDS and never waits on a global load
+//     (such a wait also waits for every copy in flight).  A pair's last
+//     stage runs only the 32-row sub-steps its rows cover.  Experts without
+//     rows get zeros.  The f32 output is written with 16-byte streaming
+//     stores of whole cache lines, which drain while the next item computes.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,12 +51,11 @@ constexpr int kSub = 32;          // contraction rows per MFMA sub-step (slabs a
 constexpr int kChunk = 128;       // contraction rows per GEMM stage (1 to 4 sub-steps)
 constexpr int kThreads = 256;
 
-// Pair table from group_sizes, built by wave 0 into LDS: for pair p (in
-// (expert, tile) order) its expert, first row and row count; returns via
-// p_base[g] the first pair of expert g (exclusive prefix, p_base[G] = total).
+// Pair table from group_sizes, built by wave 0 into LDS: expert g owns rows
+// [g_start[g], g_start[g + 1]) (clamped to the buffer) and pairs
+// [p_base[g], p_base[g + 1]) in (expert, tile) order.
 struct PairTable {
-  int* g_start;   // [G]
-  int* g_end;     // [G]
+  int* g_start;   // [G + 1]
   int* p_base;    // [G + 1]
 };
 
@@ -76,9 +78,9 @@ __device__ __forceinline__ void build_pair_table(const int* __restrict__ group_s
     const int pincl = wave_incl_scan(np);
     if (g < G) {
       t.g_start[g] = st;
-      t.g_end[g] = en;
       t.p_base[g] = pair_carry + pincl - np;
     }
+    if (g == G - 1) t.g_start[G] = en;   // the next expert would start here
     row_carry = min(__shfl(e_raw, 63, 64), M);
     pair_carry += __shfl(pincl, 63, 64);
   }
@@ -91,7 +93,7 @@ __device__ __forceinline__ void build_pair_table(const int* __restrict__ group_s
 
 // Rows [r0, r1) of pair p (its expert is g).
 __device__ __forceinline__ void pair_rows(const PairTable& t, int g, int p, int& r0, int& r1) {
-  const int s = t.g_start[g], e = t.g_end[g];
+  const int s = t.g_start[g], e = t.g_start[g + 1];
   const int tile = s / kTileM + (p - t.p_base[g]);
   r0 = max(s, tile * kTileM);
   r1 = min(e, (tile + 1) * kTileM);
@@ -115,9 +117,9 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
                                                              int K, int N, uint8_t* __restrict__ ql,
                                                              uint8_t* __restrict__ qd, float* __restrict__ sl,
                                                              float* __restrict__ sd, int* status) {
-  __shared__ int g_start[kMaxGroups], g_end[kMaxGroups], p_base[kMaxGroups + 1];
+  __shared__ int g_start[kMaxGroups + 1], p_base[kMaxGroups + 1];
   __shared__ float red[4][kPrepCols];
-  PairTable pt{g_start, g_end, p_base};
+  PairTable pt{g_start, p_base};
   // blockIdx.x = 64-column chunk (fastest, so that blocks dispatched together
   // read neighbouring strips of the same rows), blockIdx.y = pair
   build_pair_table(group_sizes, G, M, pt, blockIdx.x == 0 ? status : nullptr);
@@ -312,8 +314,8 @@ __global__ __launch_bounds__(kThreads) void dense_gather_kernel(const uint8_t* _
                                                                 int K, int N, uint8_t* __restrict__ ql,
                                                                 uint8_t* __restrict__ qd, float* __restrict__ sl,
                                                                 float* __restrict__ sd, int* status) {
-  __shared__ int g_start[kMaxGroups], g_end[kMaxGroups], p_base[kMaxGroups + 1];
-  PairTable pt{g_start, g_end, p_base};
+  __shared__ int g_start[kMaxGroups + 1], p_base[kMaxGroups + 1];
+  PairTable pt{g_start, p_base};
   build_pair_table(group_sizes, G, M, pt, blockIdx.y == 0 ? status : nullptr);
   __syncthreads();
   const int p = blockIdx.x;
@@ -352,13 +354,14 @@ constexpr int BNN = 128;                        // drhs columns (n) per block
 constexpr int kGThreads = 512;                  // 8 waves: 4 along k x 2 along n, 64 x 64 each
 constexpr int kAStage = kChunk * BMK;           // qL codes [128 rows][256 k]
 constexpr int kBStage = kChunk * BNN;           // qD codes [128 rows][128 n]
-constexpr int kStageG = kAStage + kBStage;      // 48 KiB
+constexpr int kSStage = 4 * (BMK + BNN);        // the stage's pair's scales: sL [256 k], sD [128 n]
+constexpr int kStageG = kAStage + kBStage + kSStage;
 constexpr int kStagesG = 3;
 constexpr int kLdsG = kStagesG * kStageG;
-static_assert(kLdsG + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
+static_assert(kLdsG + sizeof(int) * 2 * (kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
 constexpr int kALoadsG = kAStage / (8 * 1024);  // 1 KB wave-wide loads per wave per stage
 constexpr int kBLoadsG = kBStage / (8 * 1024);
-constexpr int kLoadsG = kALoadsG + kBLoadsG;
+constexpr int kLoadsG = kALoadsG + kBLoadsG + 1;   // + one 256-byte scale slice per wave
 
 // 16-byte chunk swizzles: the 16 lanes of a transposing read touch 8
 // consecutive rows at one chunk, and two such groups are served together.
@@ -385,25 +388,40 @@ __device__ __forceinline__ v4i widen8(const v2i& c) {
   return o;
 }
 
+// Where a wave's share of a stage's copy goes: operand codes (kALoadsG +
+// kBLoadsG 1 KB loads) and one 256-byte slice of the pair's scales (waves 0-3
+// the four sL quarters, waves 4-5 the two sD halves, waves 6-7 the sD halves
+// again, landing on the same bytes with the same values), so every wave
+// issues the same number of copies per stage.
+struct StageCopy {
+  BufRsrc ra, rb, rs;
+  uint32_t va[kALoadsG], vb[kBLoadsG];   // per-lane offsets (held by value: no array in memory)
+  uint32_t soa, sob, vs, s_lds;
+};
+
 // One 128-row stage: optionally start the copy of a later stage into `wr`,
-// then read this stage's operands from `rd` and run NS 32-row sub-steps of
-// 16 MFMAs per wave.
+// then read this stage's operands from `rd` and run its first `nsub` (of NS)
+// 32-row sub-steps of 16 MFMAs per wave.  On a pair's last stage (`last`)
+// the partial is rescaled by the pair's scales, read from this stage's slot,
+// and added to the total.
 // `wr` and `rd` are distinct ring slots; marking them __restrict__ lets the
 // compiler see that the reads cannot depend on the copy just issued, so it
 // adds no wait for it (the kernel's own wait + barrier order the ring).
 template <bool GRAD_E5M2, int NS>
 __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, bool copy,
-                                           BufRsrc ra, BufRsrc rb, const uint32_t* va, const uint32_t* vb,
-                                           uint32_t soa, uint32_t sob, int wave, const int* a_rd, const int* b_rd,
-                                           v4f (&part)[4][4]) {
+                                           const StageCopy& cp, int wave, const int* a_rd, const int* b_rd,
+                                           int nsub, bool last, int sl_rd, int sd_rd, v4f (&part)[4][4],
+                                           v4f (&tot)[4][4]) {
   if (copy) {
 #pragma unroll
-    for (int j = 0; j < kALoadsG; ++j) dma16(ra, wr + (kALoadsG * wave + j) * 1024, va[j], soa);
+    for (int j = 0; j < kALoadsG; ++j) dma16(cp.ra, wr + (kALoadsG * wave + j) * 1024, cp.va[j], cp.soa);
 #pragma unroll
-    for (int j = 0; j < kBLoadsG; ++j) dma16(rb, wr + kAStage + (kBLoadsG * wave + j) * 1024, vb[j], sob);
+    for (int j = 0; j < kBLoadsG; ++j) dma16(cp.rb, wr + kAStage + (kBLoadsG * wave + j) * 1024, cp.vb[j], cp.sob);
+    dma4(cp.rs, wr + kAStage + kBStage + cp.s_lds, cp.vs, 0);
   }
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
+    if (s >= nsub) break;     // a pair's last stage: rows past its 32-row padding are not computed
     v4i bo[4], ao[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bo[j] = widen8<GRAD_E5M2>(lds_read_tr8(rd + b_rd[j] + s * 32 * BNN));
@@ -415,6 +433,23 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
       for (int j = 0; j < 4; ++j)
         part[f][j] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, bo[j]), __builtin_bit_cast(v8bf, ao[f]), part[f][j]);
   }
+  if (last) {
+    // pair complete: total += partial * sL[k] * sD[n]
+    float slv[4];
+    v4f sdv[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) slv[f] = *reinterpret_cast<const float*>(rd + sl_rd + 64 * f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sdv[j] = *reinterpret_cast<const v4f*>(rd + sd_rd + 64 * j);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[f][j][r] = __builtin_fmaf(part[f][j][r] * slv[f], sdv[j][r], tot[f][j][r]);
+        part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      }
+  }
 }
 
 template <bool GRAD_E5M2>
@@ -425,9 +460,8 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
                       float* __restrict__ drhs) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* g_start = reinterpret_cast<int*>(smem + kLdsG);
-  int* g_end = g_start + G;
-  int* p_base = g_end + G;
-  PairTable pt{g_start, g_end, p_base};
+  int* p_base = g_start + G + 1;
+  PairTable pt{g_start, p_base};
   build_pair_table(group_sizes, G, M, pt, nullptr);
   __syncthreads();
   auto nchunks = [&](int g, int p) {
@@ -469,6 +503,9 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   for (int f = 0; f < 4; ++f) a_rd[f] = l_slot(rbase, wk * 4 + f) + 8 * (Lg & 1);
 #pragma unroll
   for (int j = 0; j < 4; ++j) b_rd[j] = kAStage + d_slot(rbase, wn * 4 + j) + 8 * (Lg & 1);
+  // the rescale's scales in a stage slot: sL[wk*64 + f*16 + lane%16], sD[wn*64 + j*16 + 4*(lane/16) + 0..3]
+  const int sl_rd = kAStage + kBStage + 4 * (wk * 64 + Lg);
+  const int sd_rd = kAStage + kBStage + 4 * BMK + 4 * (wn * 64 + 4 * (lane >> 4));
 
   // ---- copy side: the next (item, pair, chunk) to copy, stages run ahead of the compute side
   int ii = blockIdx.x, ig = 0, ikt = 0, int_ = 0, ip = 0, ip1 = 0, ic = 0, inc = 0, irows = 0;
@@ -505,6 +542,32 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < kBLoadsG; ++j) vb_i[j] = vb[j] + (uint32_t)int_ * BNN;
   };
+  // this wave's slice of the pair's scales (see StageCopy)
+  const bool s_is_l = wave < 4;
+  const int s_part = s_is_l ? wave : (wave - 4) & 1;
+  const uint32_t s_lds = (s_is_l ? 0u : 4u * BMK) + 256u * (uint32_t)s_part;
+  // The slice's source is written without a select between the copy-side
+  // tile indices (the optimizer turns such a select into one between their
+  // addresses, which pins them in scratch): per-wave multipliers, opaque to it.
+  const float* s_base = s_is_l ? sl : sd;
+  const int s_stride = __builtin_amdgcn_readfirstlane(s_is_l ? K : N);
+  const int s_mul_k = __builtin_amdgcn_readfirstlane(s_is_l ? BMK : 0);
+  const int s_mul_n = __builtin_amdgcn_readfirstlane(s_is_l ? 0 : BNN);
+  auto stage_copy = [&]() {
+    StageCopy cp;
+    cp.ra = copy_rsrc_a();
+    cp.rb = copy_rsrc_b();
+    cp.rs = make_rsrc(s_base + (size_t)ip * s_stride, 4u * (uint32_t)s_stride);
+#pragma unroll
+    for (int j = 0; j < kALoadsG; ++j) cp.va[j] = va_i[j];
+#pragma unroll
+    for (int j = 0; j < kBLoadsG; ++j) cp.vb[j] = vb_i[j];
+    cp.soa = (uint32_t)ic * kChunk * (uint32_t)K;
+    cp.sob = (uint32_t)ic * kChunk * (uint32_t)N;
+    cp.vs = 4u * (uint32_t)(ikt * s_mul_k + int_ * s_mul_n + 64 * s_part + lane);
+    cp.s_lds = s_lds;
+    return cp;
+  };
   auto advance = [&]() {
     ++tI;
     if (++ic == inc) {
@@ -521,13 +584,12 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   };
   auto issue = [&]() {          // prologue copies (nothing is read yet)
     uint8_t* St = smem + (tI % kStagesG) * kStageG;
-    const BufRsrc ra = copy_rsrc_a(), rb = copy_rsrc_b();
+    const StageCopy cp = stage_copy();
 #pragma unroll
-    for (int j = 0; j < kALoadsG; ++j)
-      dma16(ra, St + (kALoadsG * wave + j) * 1024, va_i[j], (uint32_t)ic * kChunk * (uint32_t)K);
+    for (int j = 0; j < kALoadsG; ++j) dma16(cp.ra, St + (kALoadsG * wave + j) * 1024, cp.va[j], cp.soa);
 #pragma unroll
-    for (int j = 0; j < kBLoadsG; ++j)
-      dma16(rb, St + kAStage + (kBLoadsG * wave + j) * 1024, vb_i[j], (uint32_t)ic * kChunk * (uint32_t)N);
+    for (int j = 0; j < kBLoadsG; ++j) dma16(cp.rb, St + kAStage + (kBLoadsG * wave + j) * 1024, cp.vb[j], cp.sob);
+    dma4(cp.rs, St + kAStage + kBStage + cp.s_lds, cp.vs, 0);
     advance();
   };
   seek();
@@ -550,15 +612,11 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
     const int kt = rem % kt_n, nt = rem / kt_n;
     const int p_end = __builtin_amdgcn_readfirstlane(p_base[g + 1]);
     for (int p = __builtin_amdgcn_readfirstlane(p_base[g]); p < p_end; ++p) {
-      // this pair's scales, needed when its last chunk is done
-      float slv[4];
-      v4f sdv[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) slv[f] = sl[(size_t)p * K + kt * BMK + wk * 64 + f * 16 + Lg];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sdv[j] = *reinterpret_cast<const v4f*>(sd + (size_t)p * N + nt * BNN + wn * 64 + j * 16 + 4 * (lane >> 4));
-      const int nc = __builtin_amdgcn_readfirstlane(nchunks(g, p));
+      // the pair's rows padded to 32: its last chunk runs only the sub-steps they cover
+      int pr0, pr1;
+      pair_rows(pt, g, p, pr0, pr1);
+      const int rpad = __builtin_amdgcn_readfirstlane((pr1 - pr0 + kSub - 1) / kSub * kSub);
+      const int nc = (rpad + kChunk - 1) / kChunk;
       for (int c = 0; c < nc; ++c, ++tC) {
         // stage tC landed in every wave's copy (only the copies issued after
         // it may still be in flight; other loads and stores only make the
@@ -571,32 +629,41 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
         const bool copy = ii < total;
         uint8_t* wr = smem + (tI % kStagesG) * kStageG;
         const uint8_t* rd = smem + (tC % kStagesG) * kStageG;
-        const uint32_t soa = (uint32_t)ic * kChunk * (uint32_t)K, sob = (uint32_t)ic * kChunk * (uint32_t)N;
-        tgmm_stage<GRAD_E5M2, kChunk / kSub>(wr, rd, copy, copy_rsrc_a(), copy_rsrc_b(), va_i, vb_i, soa, sob, wave,
-                                             a_rd, b_rd, part);
+        const int nsub = min(kChunk, rpad - c * kChunk) / kSub;
+        tgmm_stage<GRAD_E5M2, kChunk / kSub>(wr, rd, copy, stage_copy(), wave, a_rd, b_rd, nsub, c == nc - 1, sl_rd,
+                                             sd_rd, part, tot);
         if (copy) advance();
       }
-      // pair complete: total += partial * sL[k] * sD[n]
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tot[f][j][r] = __builtin_fmaf(part[f][j][r] * slv[f], sdv[j][r], tot[f][j][r]);
-          part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-        }
     }
-    // ---- store the tile (zeros for an expert without rows):
-    // lane owns k = wk*64 + f*16 + lane%16, n = wn*64 + j*16 + 4*(lane/16) + 0..3
+    // ---- store the tile (zeros for an expert without rows).
+    // Lane (a = lane%16, b = lane/16) holds, for each f and j, row
+    // k = wk*64 + f*16 + a and columns n = wn*64 + 16j + 4b .. +3, so lanes
+    // a and a^8 hold the two 64-byte halves of the same cache lines (j even /
+    // odd).  They swap one half (a DPP rotate by 8 within each row of 16
+    // lanes, masked to the receiving lanes) so that each store writes 8 rows
+    // x 128 contiguous bytes: streaming stores of half lines run at about
+    // half the HBM write rate of whole lines.
     float* out = drhs + ((size_t)g * K + (size_t)kt * BMK) * N + (size_t)nt * BNN;
+    const int a8 = lane & 7, hi8 = (lane >> 3) & 1;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      float* orow = out + (size_t)(wk * 64 + f * 16 + (lane & 15)) * N + wn * 64 + 4 * (lane >> 4);
+      float* orow = out + (size_t)(wk * 64 + f * 16 + a8) * N + wn * 64 + 16 * hi8 + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        __builtin_nontemporal_store(tot[f][j], reinterpret_cast<v4f*>(orow + j * 16));
-        tot[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < 2; ++m) {
+        const v4f lo = tot[f][2 * m], hi = tot[f][2 * m + 1];
+        v4f r0, r1;   // rows a8 and a8 + 8 of the 16-row block, columns 32m + 16*hi8 + 4b
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // plain scalars: bit-casting a vector element directly reads element 0
+          const int l = __builtin_bit_cast(int, (float)lo[r]), h = __builtin_bit_cast(int, (float)hi[r]);
+          r0[r] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(l, h, 0x128, 0xf, 0xc, false));
+          r1[r] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(h, l, 0x128, 0xf, 0x3, false));
+        }
+        __builtin_nontemporal_store(r0, reinterpret_cast<v4f*>(orow + 32 * m));
+        __builtin_nontemporal_store(r1, reinterpret_cast<v4f*>(orow + (size_t)8 * N + 32 * m));
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tot[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -618,7 +685,7 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 hipError_t launch_tgmm_gemm(const uint8_t* ql, const uint8_t* qd, const float* sl, const float* sd,
                             const int* group_sizes, int G, int M, int K, int N, bool grad_e5m2, float* drhs,
                             hipStream_t stream) {
-  const size_t lds = kLdsG + sizeof(int) * (3 * (size_t)G + 1);
+  const size_t lds = kLdsG + sizeof(int) * 2 * ((size_t)G + 1);
   const long long items = (long long)G * (K / BMK) * (N / BNN);
   const dim3 grid((unsigned)std::min<long long>(items, device_cu_count()));   // one resident block per CU
   if (grad_e5m2)
