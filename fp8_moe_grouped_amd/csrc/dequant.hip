@@ -4,11 +4,14 @@
 // scale[g,n])), the f32 product rounded once to bf16.
 //
 // HBM-bound (1 byte read + 2 bytes written per element).  A block covers 16
-// rows (g, k) of one expert (K is a multiple of 16) and 64 16-code chunks of
-// those rows; a thread owns one chunk column, loads its 16 scales once and
-// turns 4 rows of 16 codes into bf16 (one 16-byte load, two 16-byte stores
-// per row, all four loads in flight together).  No integer division per
-// element: the expert is one scalar division per block.
+// rows (g, k) of one expert (K is a multiple of 16) and 64 8-code chunks of
+// those rows; a thread owns one chunk column, loads its 8 scales once and
+// turns 4 rows of 8 codes into bf16 (one 8-byte load and one 16-byte store
+// per row, all four loads in flight together).  A wave's store is 1 KB of
+// contiguous output: streaming stores that leave cache lines half written
+// (16 codes per lane, two stores 32 bytes apart) run at about half the HBM
+// write rate.  No integer division per element: the expert is one scalar
+// division per block.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,46 +27,42 @@ template <bool ALIGNED>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scale, long long rows, long long K,
                                                       int N, uint16_t* __restrict__ out) {
-  const int nc_row = N >> 4;
+  const int nc_row = N >> 3;
   const int chunk = blockIdx.y * kChunksPerBlock + (threadIdx.x & 63);
   if (chunk >= nc_row) return;
   const long long rb = (long long)blockIdx.x * kRowsPerBlock;
   const long long row0 = rb + (threadIdx.x >> 6);
-  v4f s[4];
+  v4f s[2];
   if (ALIGNED) {
     const long long g = rb / K;
-    const v4f* sp = reinterpret_cast<const v4f*>(scale + (size_t)g * N + (chunk << 4));
+    const v4f* sp = reinterpret_cast<const v4f*>(scale + (size_t)g * N + (chunk << 3));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s[q] = sp[q];
+    for (int q = 0; q < 2; ++q) s[q] = sp[q];
   }
-  v4i c[4];
+  v2i c[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     if (ALIGNED || row0 + 4 * r < rows)
-      c[r] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(codes + (row0 + 4 * r) * N) + chunk);
+      c[r] = __builtin_nontemporal_load(reinterpret_cast<const v2i*>(codes + (row0 + 4 * r) * N) + chunk);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const long long row = row0 + 4 * r;
     if (!ALIGNED) {
       if (row >= rows) break;
-      const v4f* sp = reinterpret_cast<const v4f*>(scale + (size_t)(row / K) * N + (chunk << 4));
+      const v4f* sp = reinterpret_cast<const v4f*>(scale + (size_t)(row / K) * N + (chunk << 3));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s[q] = sp[q];
+      for (int q = 0; q < 2; ++q) s[q] = sp[q];
     }
-    v4i o0, o1;
+    v4i o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const uint32_t w = (uint32_t)c[r][q];
       const v2f lo = dec_e4m3x2<false>(w);
       const v2f hi = dec_e4m3x2<true>(w);
-      const uint32_t p0 = pack_bf16x2(lo[0] * s[q][0], lo[1] * s[q][1]);
-      const uint32_t p1 = pack_bf16x2(hi[0] * s[q][2], hi[1] * s[q][3]);
-      if (q < 2) { o0[2 * q] = (int)p0; o0[2 * q + 1] = (int)p1; }
-      else { o1[2 * (q - 2)] = (int)p0; o1[2 * (q - 2) + 1] = (int)p1; }
+      o[2 * q] = (int)pack_bf16x2(lo[0] * s[q][0], lo[1] * s[q][1]);
+      o[2 * q + 1] = (int)pack_bf16x2(hi[0] * s[q][2], hi[1] * s[q][3]);
     }
-    v4i* op = reinterpret_cast<v4i*>(out + row * N) + 2 * chunk;
-    __builtin_nontemporal_store(o0, op);
-    __builtin_nontemporal_store(o1, op + 1);
+    __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(out + row * N) + chunk);
   }
 }
 
@@ -75,7 +74,7 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scale, int G, long 
   if (rows == 0 || N == 0) return hipSuccess;
   // N is a multiple of 16 and G*K*N < 2^40 (checked by the caller)
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock),
-                  (unsigned)((N / 16 + kChunksPerBlock - 1) / kChunksPerBlock));
+                  (unsigned)((N / 8 + kChunksPerBlock - 1) / kChunksPerBlock));
   if (K % kRowsPerBlock == 0)
     hipLaunchKernelGGL(dequant_kernel<true>, grid, dim3(256), 0, stream, codes, scale, rows, K, (int)N, out);
   else
