@@ -419,19 +419,34 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
     for (int j = 0; j < kBLoadsG; ++j) dma16(cp.rb, wr + kAStage + (kBLoadsG * wave + j) * 1024, cp.vb[j], cp.sob);
     dma4(cp.rs, wr + kAStage + kBStage + cp.s_lds, cp.vs, 0);
   }
+  // Sub-steps are software-pipelined: the codes of sub-step s+1 are read
+  // before sub-step s's MFMAs and widened after them.
+  v4i bo[4], ao[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bo[j] = widen8<GRAD_E5M2>(lds_read_tr8(rd + b_rd[j]));
+#pragma unroll
+  for (int f = 0; f < 4; ++f) ao[f] = widen8<false>(lds_read_tr8(rd + a_rd[f]));
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (s >= nsub) break;     // a pair's last stage: rows past its 32-row padding are not computed
-    v4i bo[4], ao[4];
+    v2i cb[4], ca[4];
+    if (s + 1 < NS) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bo[j] = widen8<GRAD_E5M2>(lds_read_tr8(rd + b_rd[j] + s * 32 * BNN));
+      for (int j = 0; j < 4; ++j) cb[j] = lds_read_tr8(rd + b_rd[j] + (s + 1) * 32 * BNN);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) ao[f] = widen8<false>(lds_read_tr8(rd + a_rd[f] + s * 32 * BMK));
+      for (int f = 0; f < 4; ++f) ca[f] = lds_read_tr8(rd + a_rd[f] + (s + 1) * 32 * BMK);
+    }
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         part[f][j] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, bo[j]), __builtin_bit_cast(v8bf, ao[f]), part[f][j]);
+    if (s + 1 < NS) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bo[j] = widen8<GRAD_E5M2>(cb[j]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) ao[f] = widen8<false>(ca[f]);
+    }
   }
   if (last) {
     // pair complete: total += partial * sL[k] * sD[n]
