@@ -48,8 +48,8 @@ MEASURED_TRAFFIC_MIB = {
     "wo_gemm": ("gmm_fwd.hip", "352ce484e45786a1", 1323, 269),
     "wi_dlhs": ("dlhs.hip", "ac6a85033b161900", 2823, 269),
     "wo_dlhs": ("dlhs.hip", "ac6a85033b161900", 1427, 77),
-    "tgmm": ("tgmm.hip", "db778cbf6acd9be2", 346 + 1181, 181 + 1925),
-    "dequant": ("dequant.hip", "6f296d8865a77f01", 455, 977),
+    "tgmm": ("tgmm.hip", "daeddd02c0ed4771", 346 + 1166, 181 + 1792),
+    "dequant": ("dequant.hip", "f3cb9d24222dc290", 455, 896),
 }
 
 
