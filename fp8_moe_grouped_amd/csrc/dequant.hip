@@ -3,11 +3,12 @@
 // dequantize path bit for bit): out[g,k,n] = bf16(f32(dec(codes[g,k,n]) *
 // scale[g,n])), the f32 product rounded once to bf16.
 //
-// HBM-bound (1 byte read + 2 bytes written per element).  A block covers 16
-// rows (g, k) of one expert (K is a multiple of 16) and 64 8-code chunks of
+// HBM-bound (1 byte read + 2 bytes written per element).  A block covers 8
+// rows (g, k) of one expert (K is a multiple of 8) and 64 8-code chunks of
 // those rows; a thread owns one chunk column, loads its 8 scales once and
-// turns 4 rows of 8 codes into bf16 (one 8-byte load and one 16-byte store
-// per row, all four loads in flight together).  A wave's store is 1 KB of
+// turns 2 rows of 8 codes into bf16 (one 8-byte load and one 16-byte store
+// per row, both loads in flight together; 2 rows per thread measured faster
+// than 1 or 4 or 8).  A wave's store is 1 KB of
 // contiguous output: streaming stores that leave cache lines half written
 // (16 codes per lane, two stores 32 bytes apart) run at about half the HBM
 // write rate.  No integer division per element: the expert is one scalar
@@ -18,10 +19,11 @@
 namespace fp8gmm {
 namespace {
 
-constexpr int kRowsPerBlock = 16;
+constexpr int kRowsPerBlock = 8;
+constexpr int kRowsPerThread = kRowsPerBlock / 4;   // four waves, each on its own rows
 constexpr int kChunksPerBlock = 64;
 
-// ALIGNED: K is a multiple of 16, so a block's 16 rows belong to one expert.
+// ALIGNED: K is a multiple of kRowsPerBlock, so a block's rows belong to one expert.
 // Otherwise every row looks up its own expert (rows past the end are skipped).
 template <bool ALIGNED>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
@@ -39,13 +41,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int q = 0; q < 2; ++q) s[q] = sp[q];
   }
-  v2i c[4];
+  v2i c[kRowsPerThread];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < kRowsPerThread; ++r)
     if (ALIGNED || row0 + 4 * r < rows)
       c[r] = __builtin_nontemporal_load(reinterpret_cast<const v2i*>(codes + (row0 + 4 * r) * N) + chunk);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < kRowsPerThread; ++r) {
     const long long row = row0 + 4 * r;
     if (!ALIGNED) {
       if (row >= rows) break;
