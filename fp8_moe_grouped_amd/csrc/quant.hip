@@ -16,6 +16,8 @@
 
 namespace fp8gmm {
 
+constexpr int kCpolStream = 2;   // buffer-load cache policy: streaming (non-temporal)
+
 __device__ __forceinline__ float round_to_bf16(float v) {
   return __builtin_bit_cast(float, pack_bf16x2(v, 0.f) << 16);
 }
@@ -36,25 +38,33 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __
   const int row = blockIdx.x * 4 + wave;
   if (row >= mv) return;
   const int nch = K >> 3;
-  const v4i* src = reinterpret_cast<const v4i*>(lhs + (size_t)row * K);
+  // The row's chunks come through a buffer range that ends at the row's end:
+  // chunks past it read as zeros (no effect on the amax, never stored), so
+  // all CPL loads are issued without a branch (behind a per-chunk branch the
+  // compiler waits for each load before issuing the next).
+  const BufRsrc rsrc = make_rsrc(lhs + (size_t)row * K, (uint32_t)K * 2u);
   v4i x[CPL];
   float amax[BLOCK ? CPL : 1];
 #pragma unroll
   for (int c = 0; c < (BLOCK ? CPL : 1); ++c) amax[c] = 0.0f;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int idx = lane + 64 * c;
-    if (idx < nch) {
-      x[c] = __builtin_nontemporal_load(src + idx);
-      float& am = amax[BLOCK ? c : 0];
+  for (int c = 0; c < CPL; ++c)
+    x[c] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)lane * 16u,
+                                                                         (uint32_t)c * 1024u, kCpolStream));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = (uint32_t)x[c][e];
-        am = __builtin_fmaxf(am, __builtin_fabsf(bf16_lo(w)));
-        am = __builtin_fmaxf(am, __builtin_fabsf(bf16_hi(w)));
-      }
+  for (int c = 0; c < CPL; ++c) {
+    float& am = amax[BLOCK ? c : 0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = (uint32_t)x[c][e];
+      am = __builtin_fmaxf(am, __builtin_fabsf(bf16_lo(w)));
+      am = __builtin_fmaxf(am, __builtin_fabsf(bf16_hi(w)));
     }
   }
+  // the quotients widen the codes again instead of keeping the amax pass's
+  // widened values alive (8 registers per chunk instead of 4)
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) asm volatile("" : "+v"(x[c]));
   float sc[BLOCK ? CPL : 1];
 #pragma unroll
   for (int c = 0; c < (BLOCK ? CPL : 1); ++c) {
