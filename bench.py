@@ -49,7 +49,7 @@ MEASURED_TRAFFIC_MIB = {
     "wi_dlhs": ("dlhs.hip", "ac6a85033b161900", 2823, 269),
     "wo_dlhs": ("dlhs.hip", "ac6a85033b161900", 1427, 77),
     "tgmm": ("tgmm.hip", "daeddd02c0ed4771", 346 + 1166, 181 + 1792),
-    "dequant": ("dequant.hip", "f3cb9d24222dc290", 455, 896),
+    "dequant": ("dequant.hip", "9145e6c144a20ab6", 455, 896),
 }
 
 
