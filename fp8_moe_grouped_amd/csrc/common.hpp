@@ -152,6 +152,20 @@ __device__ __forceinline__ void wait_vmem_lds() {
   asm volatile("" ::: "memory");   // no load of the landed data may be hoisted above the wait
 }
 
+// x / s for the quantizers, from r = 1/s (correctly rounded, one division per
+// scale): q0 = x*r, the residual x - q0*s (exact through the fma), one
+// correction, and x's sign (so that -0 stays -0).  Over the quantizers' inputs
+// -- x a bf16 value with |x| <= amax, s = f32(max(amax, 1e-12) / FMAX), FMAX
+// 448 or 57344, amax finite -- the result equals the IEEE quotient wherever the
+// quotient is at least half the smallest subnormal code of the format (below
+// that both encode to zero): tests/test_div_by_scale.py checks every such pair.
+// s must be finite; callers divide directly otherwise.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): it does not
 // wait for this wave's outstanding LDS-destination loads, which is what lets
 // a copy two stages ahead stay in flight.  Callers wait for what they need

@@ -71,19 +71,35 @@ __global__ __launch_bounds__(256) void quant_rows_e4m3_kernel(const uint16_t* __
     sc[c] = __builtin_fmaxf(wave_max(amax[c]), kAmaxFloor) / kE4M3Max;   // IEEE f32 division
     if (SBF16) sc[c] = round_to_bf16(sc[c]);
   }
-  v2i* dst = reinterpret_cast<v2i*>(codes + (size_t)row * K);
+  // The quotient comes from the scale's reciprocal (div_by_scale, checked for
+  // f32 scales of this form); a bf16-rounded scale or a non-finite one (an Inf
+  // in the row) divides directly.
+  float rsc[BLOCK ? CPL : 1];
+  bool finite = !SBF16;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int idx = lane + 64 * c;
-    if (idx < nch) {
-      const float s = sc[BLOCK ? c : 0];
-      const uint32_t w0 = x[c][0], w1 = x[c][1], w2 = x[c][2], w3 = x[c][3];
-      v2i q;
-      q[0] = (int)cvt_e4m3x4(bf16_lo(w0) / s, bf16_hi(w0) / s, bf16_lo(w1) / s, bf16_hi(w1) / s);
-      q[1] = (int)cvt_e4m3x4(bf16_lo(w2) / s, bf16_hi(w2) / s, bf16_lo(w3) / s, bf16_hi(w3) / s);
-      dst[idx] = q;
-    }
+  for (int c = 0; c < (BLOCK ? CPL : 1); ++c) {
+    rsc[c] = 1.0f / sc[c];
+    finite = finite && __builtin_isfinite(sc[c]);
   }
+  v2i* dst = reinterpret_cast<v2i*>(codes + (size_t)row * K);
+  auto quantize = [&](auto fast_c) {
+    constexpr bool FAST = decltype(fast_c)::value;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lane + 64 * c;
+      if (idx < nch) {
+        const float s = sc[BLOCK ? c : 0], r = rsc[BLOCK ? c : 0];
+        auto quo = [&](float v) { return FAST ? div_by_scale(v, s, r) : v / s; };
+        const uint32_t w0 = x[c][0], w1 = x[c][1], w2 = x[c][2], w3 = x[c][3];
+        v2i q;
+        q[0] = (int)cvt_e4m3x4(quo(bf16_lo(w0)), quo(bf16_hi(w0)), quo(bf16_lo(w1)), quo(bf16_hi(w1)));
+        q[1] = (int)cvt_e4m3x4(quo(bf16_lo(w2)), quo(bf16_hi(w2)), quo(bf16_lo(w3)), quo(bf16_hi(w3)));
+        dst[idx] = q;
+      }
+    }
+  };
+  if (finite) quantize(std::true_type{});
+  else quantize(std::false_type{});
   if (lane == 0) {
     if (BLOCK) {
       const int nb = (K + 511) >> 9;

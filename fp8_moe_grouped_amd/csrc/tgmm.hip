@@ -188,30 +188,45 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
     float* sdst = is_l ? sl + (size_t)p * K : sd + (size_t)p * N;
     sdst[c0 + tid] = __builtin_fmaxf(a, kAmaxFloor) / fmax;
   }
-  // ---- quantize (f32 quotient, saturating RNE) and store the codes row-major in the pair's slab
-  uint8_t* dst = (is_l ? ql + (size_t)p * kTileM * K : qd + (size_t)p * kTileM * N) + c0 + cg * 8;
+  // ---- quantize (f32 quotient, saturating RNE) and store the codes row-major in the pair's slab.
+  // The quotient comes from the column's reciprocal (div_by_scale); a lane
+  // with a non-finite scale (an Inf in its columns) divides directly.
+  float rs[8];
+  bool finite = true;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = rr + 32 * i;
-    if (r < Rpad) {
-      float q[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        q[2 * e] = bf16_lo((uint32_t)x[i][e]) / s[2 * e];
-        q[2 * e + 1] = bf16_hi((uint32_t)x[i][e]) / s[2 * e + 1];
-      }
-      v2i w;
-      if (is_l || !GRAD_E5M2) {
-        w[0] = (int)cvt_e4m3x4(q[0], q[1], q[2], q[3]);
-        w[1] = (int)cvt_e4m3x4(q[4], q[5], q[6], q[7]);
-      } else {
-        w[0] = (int)cvt_e5m2x4(q[0], q[1], q[2], q[3]);
-        w[1] = (int)cvt_e5m2x4(q[4], q[5], q[6], q[7]);
-      }
-      if (r >= R) w = (v2i){0, 0};
-      *reinterpret_cast<v2i*>(dst + (size_t)r * cols) = w;
-    }
+  for (int e = 0; e < 8; ++e) {
+    rs[e] = 1.0f / s[e];
+    finite = finite && __builtin_isfinite(s[e]);
   }
+  uint8_t* dst = (is_l ? ql + (size_t)p * kTileM * K : qd + (size_t)p * kTileM * N) + c0 + cg * 8;
+  auto quantize = [&](auto fast_c) {
+    constexpr bool FAST = decltype(fast_c)::value;
+    auto quo = [&](float v, int e) { return FAST ? div_by_scale(v, s[e], rs[e]) : v / s[e]; };
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = rr + 32 * i;
+      if (r < Rpad) {
+        float q[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q[2 * e] = quo(bf16_lo((uint32_t)x[i][e]), 2 * e);
+          q[2 * e + 1] = quo(bf16_hi((uint32_t)x[i][e]), 2 * e + 1);
+        }
+        v2i w;
+        if (is_l || !GRAD_E5M2) {
+          w[0] = (int)cvt_e4m3x4(q[0], q[1], q[2], q[3]);
+          w[1] = (int)cvt_e4m3x4(q[4], q[5], q[6], q[7]);
+        } else {
+          w[0] = (int)cvt_e5m2x4(q[0], q[1], q[2], q[3]);
+          w[1] = (int)cvt_e5m2x4(q[4], q[5], q[6], q[7]);
+        }
+        if (r >= R) w = (v2i){0, 0};
+        *reinterpret_cast<v2i*>(dst + (size_t)r * cols) = w;
+      }
+    }
+  };
+  if (finite) quantize(std::true_type{});
+  else quantize(std::false_type{});
 }
 
 // ------------------------------------------------------------------ buffer-wide baseline
