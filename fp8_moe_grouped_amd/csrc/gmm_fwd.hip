@@ -423,7 +423,9 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
             for (int e = 0; e < 4; ++e) {
               yg[e] = (acc[i][j][4 * q + e] * sr) * sg[e];
               yu[e] = (acc[i][j + 2][4 * q + e] * sr) * su[e];
-              o[e] = yg[e] / (1.0f + __expf(-yg[e])) * yu[e];
+              // silu through the hardware reciprocal (about 1 ulp) rather than an
+              // IEEE division: the product is rounded to bf16 right after
+              o[e] = yg[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-yg[e])) * yu[e];
             }
             poq[q][0] = (int)pack_bf16x2(o[0], o[1]);
             poq[q][1] = (int)pack_bf16x2(o[2], o[3]);
