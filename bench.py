@@ -44,11 +44,11 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
 # were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "219b65fea41e470c", 2758, 77),
-    "wo_gemm": ("gmm_fwd.hip", "219b65fea41e470c", 1325, 269),
-    "wi_dlhs": ("dlhs.hip", "f9842814dfd0c577", 2828, 269),
+    "wi_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 2757, 77),
+    "wo_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 1322, 269),
+    "wi_dlhs": ("dlhs.hip", "f9842814dfd0c577", 2824, 269),
     "wo_dlhs": ("dlhs.hip", "f9842814dfd0c577", 1427, 77),
-    "tgmm": ("tgmm.hip", "0a83fb49bf493546", 346 + 1127, 181 + 1792),
+    "tgmm": ("tgmm.hip", "0a83fb49bf493546", 346 + 1139, 181 + 1792),
     "dequant": ("dequant.hip", "6ad3c03ff95eea84", 455, 896),
 }
 
