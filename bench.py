@@ -130,29 +130,129 @@ def bytes_of(d):
     }
 
 
-def cpu_baseline(d, seconds_target):
-    """The oracle as it stands, on a bounded sample: the wi forward (SwiGLU) of
-    evenly spread valid rows; returns its TFLOP/s on this host."""
-    from oracle import gmm as O
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(d, seconds_target):
+    """The oracle as it stands, on a bounded sample: the wi forward (SwiGLU) of
+    evenly spread valid rows, timed three times (median), on this host's
+    cores.  Beside it, for a fairer CPU throughput figure, the same sample
+    with the oracle's own quantization and an f32 BLAS contraction (not the
+    oracle: its products are rounded in f32)."""
+    from oracle import formats as F
+    from oracle import gmm as O
     mv = int(np.sum(d["gs"]))
     n = 128
-    while True:
+    while True:                                      # size the sample: one run ~ seconds_target / 6
         rows = np.linspace(0, mv - 1, n).astype(np.int64)
         t0 = time.time()
         O.gmm_fwd(d["lhs_wi"], d["codes_wi"], d["scale_wi"], d["gs"], swiglu_out=True, rows=rows)
         dt = time.time() - t0
-        if dt * 2 > seconds_target or n >= mv:
+        if dt * 12 > seconds_target or n >= mv:
             break
         n = min(2 * n, mv)
+    runs = []
+    for _ in range(3):
+        t0 = time.time()
+        O.gmm_fwd(d["lhs_wi"], d["codes_wi"], d["scale_wi"], d["gs"], swiglu_out=True, rows=rows)
+        runs.append(time.time() - t0)
+
+    def f32_variant():
+        lay = O.layout(d["gs"], d["M"])
+        gid = lay.group_of_rows(d["M"])[rows]
+        for g in np.unique(gid):
+            sel = rows[gid == g]
+            x = F.bf16_to_f32(d["lhs_wi"][sel])
+            s = O.row_scales(x)
+            q = F.decode(O.quantize_rows(x, s), F.E4M3).astype(np.float32)
+            c = F.decode(d["codes_wi"][g], F.E4M3).astype(np.float32)
+            y = (q @ c) * s[:, None] * d["scale_wi"][g][None, :]
+            F.f64_to_bf16_bits(O.swiglu(y[:, :2048].astype(np.float64), y[:, 2048:].astype(np.float64)))
+
+    runs32 = []
+    for _ in range(3):
+        t0 = time.time()
+        f32_variant()
+        runs32.append(time.time() - t0)
     fl = 2.0 * n * 7168 * 4096
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"wi forward + SwiGLU (K=7168, N=2x2048) of {n} of the {mv} valid rows, "
-                      f"spread over the experts; {dt:.1f}s"}
+    med, med32 = float(np.median(runs)), float(np.median(runs32))
+    return {"value": fl / med / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"wi forward + SwiGLU (K=7168, N=2x2048) of {n} of the {mv} valid rows, spread over the "
+                      f"experts; median of 3 runs ({', '.join(f'{t:.1f}' for t in runs)} s), float64 oracle",
+            "host": {"cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()},
+            "f32_blas_variant": {"value": fl / med32 / 1e12, "unit": "TFLOP/s",
+                                 "runs_s": [round(t, 2) for t in runs32],
+                                 "what": "same sample, oracle quantization, f32 BLAS contraction (not the oracle)"}}
+
+
+def sample_sclk(run_for_s, fn):
+    """Shader clock while the bench step runs back to back for about
+    run_for_s seconds: amd-smi is sampled in a second thread; returns the
+    samples (MHz) or the error."""
+    import subprocess
+    import threading
+    samples, errors = [], []
+    stop = threading.Event()
+
+    def find_clk(obj):
+        if isinstance(obj, dict):
+            for k, v in obj.items():
+                if "gfx" in str(k).lower():
+                    c = v.get("clk") if isinstance(v, dict) else None
+                    if isinstance(c, dict) and isinstance(c.get("value"), (int, float)):
+                        return float(c["value"])
+                r = find_clk(v)
+                if r is not None:
+                    return r
+        elif isinstance(obj, list):
+            for v in obj:
+                r = find_clk(v)
+                if r is not None:
+                    return r
+        return None
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                p = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                v = find_clk(json.loads(p.stdout)) if p.returncode == 0 else None
+                if v is None:
+                    errors.append((p.stderr or p.stdout)[-200:])
+                else:
+                    samples.append(v)
+            except Exception as e:   # tool missing or unparsable output: report, do not fail the bench
+                errors.append(str(e)[:200])
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.time()
+    import torch
+    while time.time() - t0 < run_for_s:
+        fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if samples:
+        return {"mhz_median": float(np.median(samples)), "samples": samples, "source": "amd-smi metric --clock"}
+    return {"mhz_median": None, "error": errors[-1] if errors else "no sample"}
 
 
 def tgmm_dense_vs_in_kernel(G, stream, lhs, dout, gs, mv):
@@ -467,6 +567,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the buffer-wide tgmm baseline")
     ap.add_argument("--no-vendor", action="store_true", help="skip the vendor dense-GEMM reference")
     ap.add_argument("--no-skinny", action="store_true", help="skip the skinny-groups (decode-like) measurement")
+    ap.add_argument("--no-sclk", action="store_true", help="skip the shader-clock sampling")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy (read MIB, write MIB) three times; used to scale "
                          "the FETCH_SIZE / WRITE_SIZE hardware counters to bytes")
@@ -593,7 +694,8 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(dom)
-    roof["traffic_unit"] = "HBM bytes per launch"
+    roof["traffic_unit"] = ("bytes per launch through the L2-fabric interface (rocprofv3 FETCH_SIZE x 2.0 + "
+                            "WRITE_SIZE, calibrated on a 1 GiB copy); Infinity Cache hits included")
 
     # bf16 arm: same scheduler, weights dequantized beforehand (not timed)
     ratio = None
@@ -621,6 +723,25 @@ def main():
         del w_wi
 
     mv = int(np.sum(d["gs"]))
+    # the tgmm with the e4m3 gradient format (the step times e5m2)
+    def timed_op(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+    t_e4 = timed_op(lambda: G.tgmm_quant(lhs_t, dout_t, gs, "e4m3", 512, out=drhs, workspace=ws_t))
+    t_e5 = timed_op(lambda: G.tgmm_quant(lhs_t, dout_t, gs, "e5m2", 512, out=drhs, workspace=ws_t))
+    tgmm_grad = {"workload": "tgmm 7168x2048 on the dropless buffer, 10 calls each after 3 warmups",
+                 "e5m2_ms": round(t_e5, 4), "e4m3_ms": round(t_e4, 4),
+                 "e5m2_gbs": round(by["tgmm"] / (t_e5 * 1e-3) / 1e9, 1),
+                 "e4m3_gbs": round(by["tgmm"] / (t_e4 * 1e-3) / 1e9, 1)}
+    sclk = None if args.no_sclk else sample_sclk(2.5, step)
     variants = None if args.no_variants else lhs_quant_variants(G, stream, lhs_wi, codes_wi, scale_wi, gs, mv)
     dense = None if args.no_dense else tgmm_dense_vs_in_kernel(G, stream, lhs_t, dout_t, gs, mv)
     micro = None if args.no_micro else pages_microbench(G, stream)
@@ -663,6 +784,8 @@ def main():
         "pages_microbench": micro,
         "lhs_quant_variants": variants,
         "tgmm_dense_baseline": dense,
+        "tgmm_grad_dtypes": tgmm_grad,
+        "sclk_during_steps": sclk,
         "vendor_dense": vendor,
         "skinny_groups": skinny,
     }

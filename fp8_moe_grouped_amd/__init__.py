@@ -422,6 +422,23 @@ def tgmm_quant(lhs, dout, group_sizes, grad_dtype="e5m2", tile_m=512, *, out=Non
     return (out, dbg_sL, dbg_sD) if debug else out
 
 
+def tgmm_workspace_codes(workspace, M, K, N, G, tile_m=512):
+    """Views of the operand codes a tgmm_quant call left in its workspace
+    (the layout the header documents): qL uint8 [Tmax, tile_m, K] and qD
+    uint8 [Tmax, tile_m, N], one slab per non-empty (expert, tile) pair in
+    (expert, tile) order; slab p holds the pair's rows in order, then zero
+    codes up to the next multiple of 32 rows."""
+    tmax = -(-M // tile_m) + G - 1
+    al = lambda x: (x + 255) // 256 * 256
+    need = workspace_bytes(OP_TGMM, M, K, N, G, tile_m)
+    if workspace.numel() < need or tmax <= 0:
+        raise ValueError("workspace too small for these sizes")
+    ql = workspace[: tmax * tile_m * K].view(tmax, tile_m, K)
+    off = al(tmax * tile_m * K)
+    qd = workspace[off: off + tmax * tile_m * N].view(tmax, tile_m, N)
+    return ql, qd
+
+
 def tgmm_dense_quant(lhs, dout, group_sizes, grad_dtype="e5m2", *, out=None, debug=False, dev_status=None,
                      workspace=None):
     """The buffer-wide backward quantization baseline (every row of the

@@ -233,9 +233,9 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
 //
 // The backward quantization the in-kernel path replaces ("MoE fp8 backward:
 // in-kernel drhs operand quantization + configurable gradient dtype", What:
-// three buffer-sized ops at the static size -- per-row lhs re-quantization,
-// dout *= the lhs row scale, per-column gradient quantization; a stale row's
-// Inf amax turns the weight gradient into Inf * 0 = NaN).  Every row of the
+// lhs rows quantized again with one scale each, that scale folded into the
+// gradient, one gradient scale per column, all over the static buffer, so an
+// Inf in a stale row reaches a column scale and the gradient becomes NaN).  Every row of the
 // buffer is read, stale rows included; the contraction then reuses the GEMM
 // below with per-pair scales 1 (lhs) and the column scale (gradient).
 

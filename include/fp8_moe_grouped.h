@@ -3,9 +3,10 @@
  * matmul library (libfp8_moe_grouped.so).
  *
  * The operations restate two pages:
- *   [P1] "MoE: native FP8 QAT for routed-expert GMMs" (maxtext PR #5969)
- *   [P3] "MoE fp8 backward: in-kernel drhs operand quantization + configurable
- *        gradient dtype" (maxtext PR #4971)
+ *   "MoE: native FP8 QAT for routed-expert GMMs" (maxtext PR #5969), with its
+ *   conversation page, and "MoE fp8 backward: in-kernel drhs operand
+ *   quantization + configurable gradient dtype" (maxtext PR #4971).
+ * Each declaration names the page and the section it follows.
  *
  * Common conventions
  * ------------------
@@ -18,14 +19,14 @@
  *   Inputs are never written and must not alias outputs or the workspace.
  * - The static ragged buffer: lhs/dout have M rows.  Rows
  *   [off_g, off_g + group_sizes[g]) belong to expert g, off_g = sum of the
- *   sizes before g (P3, What: only the tiles covered by group_sizes are
+ *   sizes before g ("MoE fp8 backward: in-kernel drhs operand quantization + configurable gradient dtype", What: only the tiles covered by group_sizes are
  *   touched).  Rows at or past sum(group_sizes) are stale: never read and,
  *   in row outputs, never written.  `group_sizes` is an int32[G] device array;
  *   a negative size counts as 0 and the running sum is clamped to M, so no
  *   access leaves the buffer.  Such repairs OR bits into *dev_status (device
  *   int32, may be NULL): FP8GMM_DEV_SUM_CLAMPED, FP8GMM_DEV_NEGATIVE_SIZE.
  * - Weight codes are e4m3fn bytes [G, K, N] (N fastest) with one f32 scale
- *   per (expert, output channel), scale[G, N] ([P1] Data flow table).
+ *   per (expert, output channel), scale[G, N] ("MoE: native FP8 QAT for routed-expert GMMs" Data flow table).
  * - Pointers to buffers with M rows may be NULL when M == 0.
  * - Host-checkable errors return before any HIP call; a failed launch returns
  *   FP8GMM_ERR_HIP.  Outputs are then unspecified.
@@ -77,7 +78,7 @@ extern "C" {
 #define FP8GMM_RHS_SCALE_FIRST 4  /* multiply by the weight scale before the activation scale */
 
 /*
- * gmm_fp8_fwd -- native FP8 forward GMM ([P1] Description: the forward GMMs
+ * gmm_fp8_fwd -- native FP8 forward GMM ("MoE: native FP8 QAT for routed-expert GMMs" Description: the forward GMMs
  * run FP8 x FP8, read the codes and per-channel scale directly and quantize
  * the activation inside the op; Implementation: one f32 scale per row over
  * the full K, max(amax, 1e-12)/448, f32 accumulation).
@@ -100,7 +101,7 @@ int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const
                 void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
 /*
- * gmm_silu_fp8 -- gmm_fp8_fwd with a fused SwiGLU epilogue for wi ([P1]
+ * gmm_silu_fp8 -- gmm_fp8_fwd with a fused SwiGLU epilogue for wi ("MoE: native FP8 QAT for routed-expert GMMs"
  * Implementation: gmm_silu_fp8).  The N = 2*I weight columns are [gate | up];
  * with y the scaled f32 GEMM result of gmm_fp8_fwd (before rounding):
  *   out[r,i] = bf16( silu(y[r,i]) * y[r,I+i] ),  silu(z) = z / (1 + exp(-z))
@@ -138,7 +139,7 @@ int gmm_silu_fp8_q(const uint8_t* aq, const float* ascale, const uint8_t* codes,
 
 /*
  * gmm_fp8_fwd_variant -- the forward with the LHS-quantization options kept for
- * benchmarks and tests ([P1] Implementation: lhs_quant_block_size 512 or the
+ * benchmarks and tests ("MoE: native FP8 QAT for routed-expert GMMs" Implementation: lhs_quant_block_size 512 or the
  * full K, lhs_f32_scale, rhs_scale_first; the bf16 scale per 512 columns with a
  * bf16 accumulator was the earlier default).  lhs_block 0 = one scale per row
  * over the full K, 512 = one scale per 512 columns (the last block may be
@@ -158,7 +159,7 @@ int gmm_fp8_fwd_variant(const void* lhs, const uint8_t* codes, const float* scal
                         void* stream);
 
 /*
- * gmm_dlhs_fp8 -- backward dLHS reading the FP8 codes ([P1] Description: the
+ * gmm_dlhs_fp8 -- backward dLHS reading the FP8 codes ("MoE: native FP8 QAT for routed-expert GMMs" Description: the
  * dLHS GMM reads the codes and dequantizes each tile on chip, no bf16 weight
  * copy is written to HBM, bit-identical to the dequant path; Implementation:
  * rhs_contract_dequant):
@@ -173,7 +174,7 @@ int gmm_dlhs_fp8(const void* dout, const uint8_t* codes, const float* scale, con
 
 /*
  * gmm_dswiglu_fp8 -- backward dLHS of the wo GMM fused with the SwiGLU
- * derivative ([P1] Implementation: gmm_dswiglu_fp8 is the wo op,
+ * derivative ("MoE: native FP8 QAT for routed-expert GMMs" Implementation: gmm_dswiglu_fp8 is the wo op,
  * _run_wo_gmm_dswiglu; its forward is gmm_fp8_fwd).  With the wo weight
  * codes [G, K, N] (K = I, the SwiGLU width; N = H, the model width), the wo
  * output gradient dout bf16 [M, N] and the wi pre-activation preact bf16
@@ -191,7 +192,7 @@ int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, 
                     int32_t* dev_status, void* stream);
 
 /*
- * tgmm_quant -- weight gradient with in-kernel operand quantization ([P3]
+ * tgmm_quant -- weight gradient with in-kernel operand quantization ("MoE fp8 backward: in-kernel drhs operand quantization + configurable gradient dtype"
  * What: moe_bwd_inkernel_quant quantizes the drhs operands per gm-tile and per
  * channel, touching only rows covered by group_sizes; bwd_quantization_dtype
  * selects e5m2 or e4m3 for the gradient).
@@ -205,6 +206,12 @@ int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, 
  * tile_m must be 512 and K a multiple of 256.  dbg_sL f32 [Tn, K] / dbg_sD f32 [Tn, N] (or NULL)
  * receive the scales of the Tn non-empty (expert, tile) pairs in (expert,
  * tile) order; Tn <= ceil(M/tile_m) + G - 1.
+ * ws: fp8gmm_workspace_bytes(FP8GMM_OP_TGMM, M, K, N, G, 512) bytes.  After
+ * the call it holds the quantized operands, readable for checks: with
+ * Tmax = ceil(M/512) + G - 1 and A(x) = x rounded up to a multiple of 256,
+ * qL u8 [Tmax][512][K] at byte 0 and qD u8 [Tmax][512][N] at byte
+ * A(Tmax*512*K); slab p (p < Tn) holds pair p's rows in order, then zero
+ * codes up to the next multiple of 32 rows (later rows are not written).
  */
 int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
                int32_t G, int32_t grad_dtype, int32_t tile_m, float* drhs, float* dbg_sL, float* dbg_sD, void* ws,
@@ -212,10 +219,12 @@ int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, in
 
 /*
  * tgmm_dense_quant -- the buffer-wide backward quantization that tgmm_quant
- * replaces, kept as a measurement baseline ([P3] What: three buffer-sized ops
- * at the static size -- the per-row lhs re-quantization, the dout *= lhs
- * row-scale multiply and the per-column gradient quantization -- and a stale
- * row's Inf amax turns the weight gradient into Inf * 0 = NaN).  Over EVERY
+ * replaces, kept as a measurement baseline ("MoE fp8 backward: in-kernel drhs
+ * operand quantization + configurable gradient dtype", What: before the
+ * in-kernel path, the lhs rows were quantized again with one scale each, that
+ * scale was folded into the gradient and the gradient got one scale per
+ * column, all over the static buffer; an Inf in a stale row then reaches a
+ * column scale and the weight gradient becomes NaN).  Over EVERY
  * row r < M of the buffer, stale rows included (amax ignores NaN):
  *   sL[r]   = f32(max(max_k |lhs[r,k]|, 1e-12) / 448),   qL = e4m3(f32(lhs / sL))
  *   d'[r,n] = f32(dout[r,n] * sL[r])
@@ -232,7 +241,7 @@ int tgmm_dense_quant(const void* lhs, const void* dout, const int32_t* group_siz
 
 /*
  * dequantize_fp8_codes -- out[g,k,n] = bf16( f32(codes[g,k,n] * scale[g,n]) )
- * ([P1] Implementation: dequantize_fp8_codes).  codes u8 [G, K, N],
+ * ("MoE: native FP8 QAT for routed-expert GMMs" Implementation: dequantize_fp8_codes).  codes u8 [G, K, N],
  * scale f32 [G, N], out bf16 [G, K, N].  N must be a multiple of 16.
  */
 int dequantize_fp8_codes(const uint8_t* codes, const float* scale, int32_t G, int64_t K, int64_t N, void* out,
@@ -242,7 +251,7 @@ int dequantize_fp8_codes(const uint8_t* codes, const float* scale, int32_t G, in
  * bf16 measurement arm: the same group schedule, copy ring, wave layout and
  * epilogues as the FP8 kernels with bf16 weights w[G, K, N] (for example the
  * output of dequantize_fp8_codes) and no activation quantization.  It is the
- * bf16 GMM the FP8 forward is compared against ([P1] Tests: kernel
+ * bf16 GMM the FP8 forward is compared against ("MoE: native FP8 QAT for routed-expert GMMs" Tests: kernel
  * microbenchmark, the bf16 arm gets a weight dequantized beforehand), and
  * gmm_bf16_dlhs(dout, dequantize_fp8_codes(codes, scale)) is bit-identical to
  * gmm_dlhs_fp8(dout, codes, scale).
@@ -261,9 +270,9 @@ int gmm_bf16_dlhs(const void* dout, const void* w, const int32_t* group_sizes, i
 
 /*
  * One routed-expert FFN on a static ragged buffer, forward and backward, as
- * the calls above chain them ([P1] Implementation: gmm_up_or_silu runs
+ * the calls above chain them ("MoE: native FP8 QAT for routed-expert GMMs" Implementation: gmm_up_or_silu runs
  * gmm_silu_fp8 for wi and _run_wo_gmm_dswiglu runs gmm_dswiglu_fp8 for wo;
- * [P3] What: both weight gradients are tgmm_quant).  x bf16 [M, H];
+ * "MoE fp8 backward: in-kernel drhs operand quantization + configurable gradient dtype" What: both weight gradients are tgmm_quant).  x bf16 [M, H];
  * wi codes [G, H, 2I] with scale [G, 2I]; wo codes [G, I, H] with scale
  * [G, H].  H and I must be multiples of 256 and at most 16384.
  *

@@ -6,9 +6,9 @@ Test infrastructure only: nothing on the product path imports this module.  Only
 
 Every function restates the method of two pages:
 
-* P1 = "MoE: native FP8 QAT for routed-expert GMMs" (maxtext PR #5969):
+* "MoE: native FP8 QAT for routed-expert GMMs" (maxtext PR #5969):
   Description ("What the new flags change"), Data flow (table), Implementation.
-* P3 = "MoE fp8 backward: in-kernel drhs operand quantization + configurable
+* "MoE fp8 backward: in-kernel drhs operand quantization + configurable
   gradient dtype" (maxtext PR #4971): What.
 
 Conventions (one reading each; the list of readings is kept with the design notes):
@@ -64,7 +64,7 @@ class Layout:
 
 
 def layout(group_sizes, M: int) -> Layout:
-    """Group offsets from ``group_sizes`` (P3, What: the in-kernel path touches
+    """Group offsets from ``group_sizes`` ("MoE fp8 backward: in-kernel drhs operand quantization + configurable gradient dtype", What: the in-kernel path touches
     only the tiles covered by group_sizes).  Negative sizes are treated as 0 and
     the running sum is clamped to the static row count M, so no row index ever
     leaves the buffer."""
@@ -83,7 +83,7 @@ def layout(group_sizes, M: int) -> Layout:
 
 def row_scales(x_f32: np.ndarray) -> np.ndarray:
     """One f32 scale per activation row over the whole K axis:
-    ``s = max(amax, 1e-12) / 448`` evaluated in f32 (P1, Implementation: LHS
+    ``s = max(amax, 1e-12) / 448`` evaluated in f32 ("MoE: native FP8 QAT for routed-expert GMMs", Implementation: LHS
     quantization options, lhs_f32_scale; the native forward always uses the full
     K with an f32 scale)."""
     x = np.asarray(x_f32, dtype=np.float32)
@@ -92,7 +92,7 @@ def row_scales(x_f32: np.ndarray) -> np.ndarray:
 
 
 def quantize_rows(x_f32: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """e4m3fn codes of ``x / s`` with the quotient rounded to f32 first (P1,
+    """e4m3fn codes of ``x / s`` with the quotient rounded to f32 first ("MoE: native FP8 QAT for routed-expert GMMs",
     Description: the forward quantizes the activation inside the kernel)."""
     q = (np.asarray(x_f32, np.float32) / np.asarray(s, np.float32)[:, None]).astype(np.float32)
     return F.encode(q, F.E4M3)
@@ -126,21 +126,21 @@ class FwdResult:
 
 
 def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
-    """``silu(gate) * up`` in float64, silu(z) = z / (1 + exp(-z)) (P1,
+    """``silu(gate) * up`` in float64, silu(z) = z / (1 + exp(-z)) ("MoE: native FP8 QAT for routed-expert GMMs",
     Implementation: gmm_silu_fp8 is wi with a fused SwiGLU)."""
     with np.errstate(over="ignore"):
         return gate / (1.0 + np.exp(-gate)) * up
 
 
 def gmm_fwd(lhs_bits, codes, scale, group_sizes, *, swiglu_out=False, rows=None) -> FwdResult:
-    """Native FP8 forward GMM (P1, Description and Data flow table: wi/wo run
+    """Native FP8 forward GMM ("MoE: native FP8 QAT for routed-expert GMMs", Description and Data flow table: wi/wo run
     FP8 x FP8 with f32 accumulation, read the codes and per-channel scale, and
     quantize the activation rows in the kernel).
 
     ``rows``: optional subset of buffer rows to evaluate (each row is
     independent given its own scale); default all valid rows.  With
     ``swiglu_out`` the N columns are ``[gate | up]`` and the output is
-    ``bf16(silu(gate) * up)`` of width N/2 (P1, Implementation: gmm_silu_fp8).
+    ``bf16(silu(gate) * up)`` of width N/2 ("MoE: native FP8 QAT for routed-expert GMMs", Implementation: gmm_silu_fp8).
     """
     lhs_bits = np.asarray(lhs_bits)
     M, K = lhs_bits.shape
@@ -175,7 +175,7 @@ def gmm_fwd(lhs_bits, codes, scale, group_sizes, *, swiglu_out=False, rows=None)
 
 def dequantize(codes, scale) -> np.ndarray:
     """``bf16(f32(dec(code) * scale))`` for ``codes[G,K,N]`` and ``scale[G,N]``
-    (P1, Implementation: dequantize_fp8_codes; the f32 product rounded once to
+    ("MoE: native FP8 QAT for routed-expert GMMs", Implementation: dequantize_fp8_codes; the f32 product rounded once to
     bf16).  Returns bf16 bit patterns [G, K, N]."""
     w32 = F.decode(codes, F.E4M3).astype(np.float32) * np.asarray(scale, np.float32)[:, None, :]
     return F.f64_to_bf16_bits(w32.astype(np.float32).astype(np.float64))
@@ -194,7 +194,7 @@ class DlhsResult:
 
 def gmm_dlhs(dout_bits, codes, scale, group_sizes, *, rows=None) -> DlhsResult:
     """Backward dLHS: ``dlhs[r, k] = bf16(sum_n dout[r, n] * w[g, k, n])`` with
-    ``w = dequantize(codes, scale)`` (P1, Description: the backward dLHS GMM
+    ``w = dequantize(codes, scale)`` ("MoE: native FP8 QAT for routed-expert GMMs", Description: the backward dLHS GMM
     reads the codes and dequantizes each tile, bit-identical to the dequant
     path; Implementation: the rhs_contract_dequant path).  The sum over n is
     float64."""
@@ -234,7 +234,7 @@ class TgmmTile:
 def tgmm_tiles(group_sizes, M: int, tile_m: int) -> list[TgmmTile]:
     """Non-empty (expert, gm-tile) pairs in (expert, tile) order.  Tiles are
     aligned to the buffer and intersected with each expert's rows, so a tile
-    that straddles an expert boundary gives one entry per expert (P3, What:
+    that straddles an expert boundary gives one entry per expert ("MoE fp8 backward: in-kernel drhs operand quantization + configurable gradient dtype", What:
     per-gm-tile-per-channel quantization that touches only the tiles covered
     by group_sizes)."""
     lay = layout(group_sizes, M)
@@ -280,7 +280,7 @@ def tgmm_quant(lhs_bits, dout_bits, group_sizes, grad_fmt: str, tile_m: int = 51
     ``drhs[g] = sum_t (sum_{r in T} dec(qL[r,:])^T dec(qD[r,:])) * (sL[t] x sD[t])``
     where for each non-empty (expert, tile) pair T the lhs is quantized to e4m3
     with one scale per lhs channel and dout to the gradient format with one
-    scale per dout channel, both over T's rows only (P3, What:
+    scale per dout channel, both over T's rows only ("MoE fp8 backward: in-kernel drhs operand quantization + configurable gradient dtype", What:
     moe_bwd_inkernel_quant and bwd_quantization_dtype).  The tile sums are exact
     integer sums; scaling and the sum over tiles are float64, rounded once to
     f32.  An expert without rows gets exact zeros.
@@ -323,7 +323,7 @@ def tgmm_quant(lhs_bits, dout_bits, group_sizes, grad_fmt: str, tile_m: int = 51
 
 def dswiglu(dprod: np.ndarray, gate: np.ndarray, up: np.ndarray):
     """Gradients of ``silu(gate) * up`` with respect to gate and up, given the
-    gradient ``dprod`` of the product, in float64 (P1, Implementation:
+    gradient ``dprod`` of the product, in float64 ("MoE: native FP8 QAT for routed-expert GMMs", Implementation:
     gmm_dswiglu_fp8 is the wo op whose backward carries the SwiGLU derivative;
     the derivative itself is calculus on the forward SwiGLU above).
 
@@ -348,7 +348,7 @@ class DswigluResult:
 
 
 def gmm_dswiglu(dout_bits, codes, scale, group_sizes, preact_bits, *, rows=None) -> DswigluResult:
-    """wo backward dLHS with the SwiGLU derivative fused after it (P1,
+    """wo backward dLHS with the SwiGLU derivative fused after it ("MoE: native FP8 QAT for routed-expert GMMs",
     Implementation: gmm_dswiglu_fp8 for wo; _run_wo_gmm_dswiglu).
 
     ``codes``/``scale`` are the wo weight ``[G, I, H]``; ``dout`` is the wo
@@ -396,8 +396,8 @@ class FfnResult:
 def moe_ffn(x_bits, wi_codes, wi_scale, wo_codes, wo_scale, group_sizes, dy_bits, grad_fmt: str,
             tile_m: int = 512) -> FfnResult:
     """Forward and backward of one routed-expert FFN on a static ragged buffer
-    (P1, Implementation: gmm_up_or_silu runs gmm_silu_fp8 for wi and
-    _run_wo_gmm_dswiglu runs gmm_dswiglu_fp8 for wo; P3, What: both weight
+    ("MoE: native FP8 QAT for routed-expert GMMs", Implementation: gmm_up_or_silu runs gmm_silu_fp8 for wi and
+    _run_wo_gmm_dswiglu runs gmm_dswiglu_fp8 for wo; "MoE fp8 backward: in-kernel drhs operand quantization + configurable gradient dtype", What: both weight
     gradients are tgmm with in-kernel operand quantization).
 
     x ``[M, H]``, wi ``[G, H, 2I]``, wo ``[G, I, H]``, dy ``[M, H]`` (the
@@ -437,8 +437,8 @@ class VariantResult(FwdResult):
 def gmm_fwd_variant(lhs_bits, codes, scale, group_sizes, *, block: int = 0, scale_bf16: bool = False,
                     acc_bf16: bool = False, rhs_scale_first: bool = False, rows=None) -> VariantResult:
     """The forward's LHS-quantization options kept as ops-level arguments for
-    benchmarks and tests (P1, Implementation: lhs_quant_block_size 512 or the
-    full K, lhs_f32_scale, rhs_scale_first; P2 review thread on the defaults:
+    benchmarks and tests ("MoE: native FP8 QAT for routed-expert GMMs", Implementation: lhs_quant_block_size 512 or the
+    full K, lhs_f32_scale, rhs_scale_first; review thread on the conversation page of "MoE: native FP8 QAT for routed-expert GMMs" on the defaults:
     a bf16 scale per 512-column block with a bf16 accumulator was the earlier
     default).
 
@@ -505,7 +505,7 @@ def gmm_fwd_variant(lhs_bits, codes, scale, group_sizes, *, block: int = 0, scal
 
 def fake_qat_reference(lhs_bits, codes, scale, group_sizes, rows=None) -> np.ndarray:
     """What the quantized forward approximates: the bf16 activations times the
-    weights code * scale, exactly (float64), per valid row (P1, Why: fake QAT
+    weights code * scale, exactly (float64), per valid row ("MoE: native FP8 QAT for routed-expert GMMs", Why: fake QAT
     runs bf16 GMMs on dequantized weights)."""
     lhs_bits = np.asarray(lhs_bits)
     M = lhs_bits.shape[0]
@@ -525,10 +525,13 @@ def fake_qat_reference(lhs_bits, codes, scale, group_sizes, rows=None) -> np.nda
 
 def tgmm_dense(lhs_bits, dout_bits, group_sizes, grad_fmt: str, k_cols=None, n_cols=None) -> TgmmResult:
     """The buffer-wide backward quantization that the in-kernel tgmm replaces
-    (P3, What: three buffer-sized ops at the buffer's static size -- the
-    per-row lhs re-quantize, the drhs_dout *= lhs.scale multiply and the
-    per-N cotangent quantize; a stale row's Inf amax turns the weight
-    gradient into Inf * 0 = NaN).
+    ("MoE fp8 backward: in-kernel drhs operand quantization + configurable
+    gradient dtype", What).  That page describes three operations sized by the
+    static buffer rather than by the valid rows: each lhs row is quantized
+    again with its own scale, that row scale is multiplied into the gradient,
+    and the gradient gets one scale per output column.  Because stale rows take
+    part, an infinite value in one of them makes a column scale infinite, and
+    the rescaled product of an infinite scale with a zero code is NaN.
 
     Over every row of the static buffer, stale rows included:
       sL[r]   = f32(max(amax_k |lhs[r,k]|, 1e-12) / 448),  qL = e4m3(f32(lhs / sL))

@@ -1,5 +1,7 @@
 """GPU parity of the backward ops (gmm_dlhs_fp8, tgmm_quant) and of the bf16
 measurement arm against the CPU oracle, through the C ABI."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -70,18 +72,45 @@ def test_dlhs_config0_shape():
     print(f"config0 dlhs: normwise {err[0]:.2e}")
 
 
-@pytest.mark.parametrize("op", ["dlhs_wi", "dlhs_wo"])
-def test_dlhs_config3_sampled(op):
+#: config-3 dLHS rows are checked in contiguous chunks (each a few tens of
+#: seconds of oracle time)
+CFG3_CHUNKS = {"dlhs_wi": 6, "dlhs_wo": 4}
+
+
+@functools.lru_cache(maxsize=None)
+def _cfg3_dlhs(op):
+    """Inputs and the GPU's result of one config-3 dLHS, computed once per session."""
     d = W.make(3, op)
-    lay = O.layout(d["group_sizes"], d["M"])
-    r = np.random.default_rng(3)
-    rows = set(r.choice(lay.valid, 256, replace=False).tolist())
-    for g in range(len(d["group_sizes"])):
-        if lay.end[g] > lay.start[g]:
-            rows.update({int(lay.start[g]), int(lay.end[g]) - 1})
-    err, st = check_dlhs(d, rows=np.array(sorted(rows)))
+    out, st = run_dlhs(d)
+    return d, out, st
+
+
+@pytest.mark.parametrize("op,chunk", [(op, c) for op in ("dlhs_wi", "dlhs_wo") for c in range(CFG3_CHUNKS[op])])
+def test_dlhs_config3_all_rows(op, chunk):
+    """The dropless shape: every valid row against the oracle (bf16 rule)."""
+    d, out, st = _cfg3_dlhs(op)
     assert st == 0
-    print(f"config3 {op}: normwise {err[0]:.2e} ratio {err[1]:.3f}")
+    got = bf16_np(out)
+    lay = O.layout(d["group_sizes"], d["M"])
+    rows = np.array_split(np.arange(lay.valid), CFG3_CHUNKS[op])[chunk]
+    res = O.gmm_dlhs(d["dout"], d["codes"], d["scale"], d["group_sizes"], rows=rows)
+    err = check_bf16(got[rows], res.y, res.absum, res.group, d["N"] * 2.0 ** -24, f"config3 {op}")
+    assert np.all(got[lay.valid:] == SENTINEL), "rows past the valid prefix were written"
+    print(f"config3 {op} rows {rows[0]}..{rows[-1]}: normwise {err[0]:.2e} ratio {err[1]:.3f}")
+
+
+@pytest.mark.parametrize("op", ["dlhs_wi", "dlhs_wo"])
+def test_dlhs_config3_bit_identity(op):
+    """The whole config-3 dLHS from the codes equals, bit for bit, the same
+    main loop fed with dequantize_fp8_codes' bf16 weights: the on-chip tiles
+    are the standalone dequantization."""
+    import fp8_moe_grouped_amd as G
+    d, out, _ = _cfg3_dlhs(op)
+    w = G.dequantize_fp8_codes(dev(d["codes"]), dev(d["scale"]))
+    ref = sentinel(*out.shape)
+    G.gmm_bf16_dlhs(dev(d["dout"]), w, dev(d["group_sizes"]), out=ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "dLHS tiles differ from dequantize_fp8_codes"
 
 
 def test_dlhs_edges_and_stale_tail():
@@ -173,13 +202,45 @@ def test_bf16_forward_arm(config, N, silu):
 
 # ---------------------------------------------------------------- tgmm
 
-def run_tgmm(lhs, dout, gs, grad, debug=True):
+def run_tgmm(lhs, dout, gs, grad, debug=True, ws_out=None):
+    """Runs tgmm_quant; with ``ws_out`` (a list) the operand code slabs the
+    call left in its workspace are appended to it as host arrays (qL, qD)."""
     import fp8_moe_grouped_amd as G
+    M, K = lhs.shape
+    N = dout.shape[1]
+    Gn = len(gs)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(G.workspace_bytes(G.OP_TGMM, M, K, N, Gn, 512), 1), dtype=torch.uint8, device="cuda")
     res = G.tgmm_quant(dev(lhs), dev(dout), dev(np.asarray(gs, np.int32)), grad, 512, debug=debug,
-                       dev_status=status)
+                       dev_status=status, workspace=ws)
     torch.cuda.synchronize()
+    if ws_out is not None:
+        ql, qd = G.tgmm_workspace_codes(ws, M, K, N, Gn)
+        ws_out.extend([ql.cpu().numpy(), qd.cpu().numpy()])
     return res, int(status.item())
+
+
+def check_tgmm_codes(lhs, dout, gs, grad, ql, qd, k_cols=None, n_cols=None):
+    """Every non-empty (expert, tile) pair's operand codes in the workspace
+    slabs equal the oracle's per-tile quantization bit for bit (the rows of
+    the pair, then zero codes up to the next multiple of 32 rows); with
+    k_cols / n_cols only those columns (a column's codes depend on that column
+    alone).  Returns the number of pairs checked."""
+    gfmt = F.E5M2 if grad == "e5m2" else F.E4M3
+    kc = slice(None) if k_cols is None else k_cols
+    nc = slice(None) if n_cols is None else n_cols
+    tiles = O.tgmm_tiles(gs, lhs.shape[0], 512)
+    for i, tl in enumerate(tiles):
+        R = tl.row1 - tl.row0
+        Rpad = -(-R // 32) * 32
+        xl = F.bf16_to_f32(lhs[tl.row0:tl.row1][:, kc])
+        xd = F.bf16_to_f32(dout[tl.row0:tl.row1][:, nc])
+        qL = O.quantize_cols(xl, O.column_scales(xl, 448.0), F.E4M3)
+        qD = O.quantize_cols(xd, O.column_scales(xd, F.FMAX[gfmt]), gfmt)
+        assert np.array_equal(ql[i, :R][:, kc], qL), f"lhs codes of pair {i} (expert {tl.group}) differ"
+        assert np.array_equal(qd[i, :R][:, nc], qD), f"{grad} gradient codes of pair {i} (expert {tl.group}) differ"
+        assert not ql[i, R:Rpad][:, kc].any() and not qd[i, R:Rpad][:, nc].any(), f"pair {i}: padding rows not zero"
+    return len(tiles)
 
 
 def _tgmm_small(seed, M=1500, K=256, N=128):
@@ -193,7 +254,9 @@ def _tgmm_small(seed, M=1500, K=256, N=128):
 def test_tgmm_small_full(grad):
     lhs, dout = _tgmm_small(5)
     gs = [0, 300, 700, 0, 1, 400, 0]          # boundaries inside tiles, empty first/last experts
-    (drhs, sL, sD), st = run_tgmm(lhs, dout, gs, grad)
+    slabs = []
+    (drhs, sL, sD), st = run_tgmm(lhs, dout, gs, grad, ws_out=slabs)
+    assert check_tgmm_codes(lhs, dout, gs, grad, *slabs) == 6
     ref = O.tgmm_quant(lhs, dout, gs, grad, 512)
     Tn = len(ref.tiles)
     assert np.array_equal(sL.cpu().numpy()[:Tn], ref.sL) and np.array_equal(sD.cpu().numpy()[:Tn], ref.sD)
@@ -219,31 +282,51 @@ def test_tgmm_stale_tail_and_status():
     assert st == 3
 
 
+@functools.lru_cache(maxsize=None)
+def _cfg4_tgmm(grad):
+    """Inputs, the GPU's gradient, scales and operand code slabs of the
+    config-4 tgmm (computed once per session and gradient format)."""
+    d = W.make(4, "tgmm")
+    slabs = []
+    (drhs, sL, sD), st = run_tgmm(d["lhs"], d["dout"], d["group_sizes"], grad, ws_out=slabs)
+    return d, drhs, sL.cpu().numpy(), sD.cpu().numpy(), slabs[0], slabs[1], st
+
+
 @pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
 def test_tgmm_config4_sampled(grad):
-    d = W.make(4, "tgmm")
-    (drhs, sL, sD), st = run_tgmm(d["lhs"], d["dout"], d["group_sizes"], grad)
+    """The dropless buffer (7168 x 2048 per expert): every scale of every
+    (expert, tile) pair bit for bit, and the f32 gradient on 128 x 128 sampled
+    (k, n) columns of every expert against the oracle's exact sums."""
+    d, drhs, sL, sD, _, _, st = _cfg4_tgmm(grad)
     assert st == 0
+    gfmt = F.E5M2 if grad == "e5m2" else F.E4M3
+    tiles = O.tgmm_tiles(d["group_sizes"], d["M"], 512)
+    for j, tl in enumerate(tiles):
+        xl = F.bf16_to_f32(d["lhs"][tl.row0:tl.row1])
+        xd = F.bf16_to_f32(d["dout"][tl.row0:tl.row1])
+        assert np.array_equal(sL[j], O.column_scales(xl, 448.0)), f"sL of pair {j}"
+        assert np.array_equal(sD[j], O.column_scales(xd, F.FMAX[gfmt])), f"sD of pair {j}"
     r = np.random.default_rng(7)
-    kc = np.sort(r.choice(d["K"], 48, replace=False))
-    nc = np.sort(r.choice(d["N"], 48, replace=False))
+    kc = np.sort(r.choice(d["K"], 128, replace=False))
+    nc = np.sort(r.choice(d["N"], 128, replace=False))
     ref = O.tgmm_quant(d["lhs"], d["dout"], d["group_sizes"], grad, 512, k_cols=kc, n_cols=nc)
     got = drhs[:, torch.from_numpy(kc).cuda()][:, :, torch.from_numpy(nc).cuda()].cpu().numpy()
     lay = O.layout(d["group_sizes"], d["M"])
     tot, per = check_f32(got, ref.drhs_f64, ref.absum, None, np.minimum(lay.end - lay.start, 512), "tgmm cfg4")
-    Tn = len(ref.tiles)
-    assert np.array_equal(sL.cpu().numpy()[:Tn][:, kc], ref.sL)
-    assert np.array_equal(sD.cpu().numpy()[:Tn][:, nc], ref.sD)
-    # every channel's scale (not only the sampled ones), straight from the oracle's definition
-    for i, tl in enumerate(ref.tiles[:: max(1, Tn // 8)]):
-        j = ref.tiles.index(tl)
-        xl = F.bf16_to_f32(d["lhs"][tl.row0:tl.row1])
-        assert np.array_equal(sL.cpu().numpy()[j], O.column_scales(xl, 448.0))
     empty = np.nonzero(np.asarray(d["group_sizes"]) == 0)[0]
     for g in empty:
         assert not torch.any(drhs[int(g)] != 0)
     assert torch.isfinite(drhs).all()
-    print(f"tgmm config4 {grad}: rel fro {tot:.2e} (max per expert {per:.2e})")
+    print(f"tgmm config4 {grad}: {len(tiles)} pairs, rel fro {tot:.2e} (max per expert {per:.2e})")
+
+
+@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
+def test_tgmm_config4_codes(grad):
+    """The dropless buffer: the lhs and gradient codes of every (expert, tile)
+    pair, every row and column, bit for bit against the oracle."""
+    d, _, _, _, ql, qd, _ = _cfg4_tgmm(grad)
+    n = check_tgmm_codes(d["lhs"], d["dout"], d["group_sizes"], grad, ql, qd)
+    print(f"tgmm config4 {grad}: codes of {n} pairs bit-exact")
 
 
 @pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
@@ -265,8 +348,10 @@ def test_tgmm_every_code(grad):
     lhs, nl = column_block(F.E4M3, K, 3)
     dout, nd = column_block(gfmt, N, 5)
     assert nl == 254 and nd == (248 if grad == "e5m2" else 254)
-    (drhs, sL, sD), st = run_tgmm(lhs, dout, [M], grad)
+    slabs = []
+    (drhs, sL, sD), st = run_tgmm(lhs, dout, [M], grad, ws_out=slabs)
     assert st == 0
+    assert check_tgmm_codes(lhs, dout, [M], grad, *slabs) == 1
     ref = O.tgmm_quant(lhs, dout, [M], grad, 512)
     assert np.all(ref.sL == 1.0) and np.all(ref.sD == 1.0)
     assert np.array_equal(sL.cpu().numpy()[:1], ref.sL) and np.array_equal(sD.cpu().numpy()[:1], ref.sD)

@@ -1,5 +1,7 @@
 """GPU parity of the native FP8 forward (gmm_fp8_fwd, gmm_silu_fp8) and of
 dequantize_fp8_codes against the CPU oracle, through the C ABI."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -81,25 +83,39 @@ def test_wo_config2():
     print(f"config2 wo: normwise {err[0]:.2e}, ratio {err[1]:.3f}")
 
 
-# ---------------------------------------------------------------- config 3 (sampled rows)
+# ---------------------------------------------------------------- config 3 (every valid row)
 
-def _sample_rows(gs, M, n_random, seed):
-    lay = O.layout(gs, M)
-    r = np.random.default_rng(seed)
-    rows = set(r.choice(lay.valid, n_random, replace=False).tolist())
-    for g in range(len(gs)):
-        if lay.end[g] > lay.start[g]:
-            rows.update({int(lay.start[g]), int(lay.end[g]) - 1})
-    return np.array(sorted(rows))
+#: the valid rows of the dropless buffer are checked in contiguous chunks, so
+#: that no single test spends more than a few tens of seconds in the oracle
+CFG3_CHUNKS = {"wi": 6, "wo": 8}
 
 
-@pytest.mark.parametrize("op", ["wi", "wo"])
-def test_config3_sampled(op):
+@functools.lru_cache(maxsize=None)
+def _cfg3_fwd(op):
+    """Inputs and the GPU's outputs (bf16 result, activation codes and row
+    scales) of one config-3 forward, computed once per session."""
     d = W.make(3, op)
-    rows = _sample_rows(d["group_sizes"], d["M"], 384, 7)
-    err, st = check_fwd(d, op == "wi", rows=rows)
+    return (d,) + run_fwd(d, op == "wi")
+
+
+@pytest.mark.parametrize("op,chunk", [(op, c) for op in ("wi", "wo") for c in range(CFG3_CHUNKS[op])])
+def test_config3_all_rows(op, chunk):
+    """The DeepSeek-V3-like dropless shape (19,661 of 32,768 rows valid,
+    Zipf-skewed experts, garbage tail): every valid row's activation codes and
+    scale bit for bit, and every output element against the bf16 rule."""
+    d, out, codes, scales, st = _cfg3_fwd(op)
     assert st == 0
-    print(f"config3 {op}: {len(rows)} sampled rows, normwise {err[0]:.2e}, ratio {err[1]:.3f}")
+    lay = O.layout(d["group_sizes"], d["M"])
+    rows = np.array_split(np.arange(lay.valid), CFG3_CHUNKS[op])[chunk]
+    swiglu = op == "wi"
+    res = O.gmm_fwd(d["lhs"], d["codes"], d["scale"], d["group_sizes"], swiglu_out=swiglu, rows=rows)
+    assert np.array_equal(codes[rows], res.act_codes), "activation codes differ"
+    assert np.array_equal(scales[rows], res.act_scale), "activation scales differ"
+    extra = swiglu_tol(res, d["N"] // 2) if swiglu else None
+    err = check_bf16(out[rows], res.out_f64, res.absum if not swiglu else np.zeros_like(res.out_f64),
+                     res.group, C_ACC_FP8, f"config3 {op}", extra_tol=extra)
+    assert np.all(out[lay.valid:] == SENTINEL), "rows past the valid prefix were written"
+    print(f"config3 {op} rows {rows[0]}..{rows[-1]}: normwise {err[0]:.2e}, ratio {err[1]:.3f}")
 
 
 # ---------------------------------------------------------------- dequant
@@ -111,6 +127,22 @@ def test_dequant_bit_exact(config, op):
     out = G.dequantize_fp8_codes(dev(d["codes"]), dev(d["scale"]))
     torch.cuda.synchronize()
     assert np.array_equal(bf16_np(out), O.dequantize(d["codes"], d["scale"]))
+
+
+@pytest.mark.parametrize("which", ["wi", "wo"])
+def test_dequant_config3_bit_exact(which):
+    """The dropless shape's weights (wi codes [32, 7168, 4096], wo codes
+    [32, 2048, 7168]) dequantized in one call; every element against the
+    oracle, expert by expert."""
+    import fp8_moe_grouped_amd as G
+    sh = W.SHAPES[3]
+    K, N, stream = (sh["K_wi"], sh["N_wi"], W.W_WI) if which == "wi" else (sh["K_wo"], sh["N_wo"], W.W_WO)
+    codes, scale = W.weights(3, stream, sh["G"], K, N)
+    out = G.dequantize_fp8_codes(dev(codes), dev(scale))
+    torch.cuda.synchronize()
+    for g in range(sh["G"]):
+        got = bf16_np(out[g])
+        assert np.array_equal(got, O.dequantize(codes[g:g + 1], scale[g:g + 1])[0]), f"expert {g} differs"
 
 
 def test_dequant_all_codes_and_scales():

@@ -125,9 +125,9 @@ def test_fake_qat_reference_matches_torch_dequant():
 
 def test_pages_ordering_against_the_rollout_reading():
     """The pages compare the forward modes by their distance to the FP8
-    rollout's MoE kernel (P2 review thread on the defaults: full-K f32 scale
+    rollout's MoE kernel (review thread on the conversation page of "MoE: native FP8 QAT for routed-expert GMMs" on the defaults: full-K f32 scale
     with f32 accumulation 0.0131, fake QAT 0.0468, a bf16 scale per 512
-    columns with a bf16 accumulator 0.0637; P1, Why: the native forward
+    columns with a bf16 accumulator 0.0637; "MoE: native FP8 QAT for routed-expert GMMs", Why: the native forward
     matches what the rollout computes).  With the rollout read as per-row
     full-K f32 quantization with f32 accumulation, the same ordering appears
     on activations with 1% outliers x50 (K = 2048): fake QAT (the exact
