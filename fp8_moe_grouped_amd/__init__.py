@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libfp8_moe_grouped.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8_moe_grouped.h")
 
 OK = 0
-ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = -1, -2, -3, -4, -5, -6
+ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 32 << 20
 DEV_SUM_CLAMPED, DEV_NEGATIVE_SIZE = 1, 2
 E4M3, E5M2 = 0, 1
 (OP_FWD, OP_SILU, OP_DLHS, OP_TGMM, OP_BF16_FWD, OP_BF16_DLHS, OP_FFN_FWD, OP_FFN_BWD, OP_FWD_VARIANT,
@@ -47,6 +48,7 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "gmm_fp8_fwd": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P, _P],
+    "gmm_fp8_fwd_noalloc": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P],
     "gmm_silu_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P],
     "gmm_dlhs_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _SZ, _P, _P],
     "tgmm_quant": [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P],
@@ -183,6 +185,27 @@ def gmm_fp8_fwd(lhs, codes, scale, group_sizes, *, out=None, debug=False, dev_st
     """Native FP8 forward GMM; returns bf16 [M, N] (and, with debug, the
     activation codes [M, K] and row scales [M] the GEMM consumed)."""
     return _fwd("gmm_fp8_fwd", OP_FWD, lhs, codes, scale, group_sizes, out, debug, dev_status, workspace, False)
+
+
+def gmm_fp8_fwd_noalloc(lhs, codes, scale, group_sizes, *, out=None, dev_status=None):
+    """gmm_fp8_fwd through the allocation-free entry point: the library keeps
+    the quantized activations in its fixed per-GPU scratch (the call itself
+    allocates nothing; only ``out``, if not given, is allocated here).
+    Returns bf16 [M, N]."""
+    _req(lhs, "lhs", torch.bfloat16, 2)
+    _req(codes, "codes", torch.uint8, 3)
+    _req(scale, "scale", torch.float32, 2)
+    _req(group_sizes, "group_sizes", torch.int32, 1)
+    dev = _same_device(lhs, codes, scale, group_sizes)
+    M, K = lhs.shape
+    G, K2, N = codes.shape
+    if K2 != K or tuple(scale.shape) != (G, N) or group_sizes.shape[0] != G:
+        raise ValueError("shape mismatch")
+    out = _out(out, (M, N), torch.bfloat16, dev, "out")
+    with torch.cuda.device(dev):
+        _call("gmm_fp8_fwd_noalloc", _ptr(lhs), _ptr(codes), _ptr(scale), _ptr(group_sizes), M, K, N, G, _ptr(out),
+              _ptr(dev_status), _stream(dev))
+    return out
 
 
 def gmm_silu_fp8(lhs, codes, scale, group_sizes, *, out=None, preact=None, debug=False, dev_status=None,

@@ -3,10 +3,19 @@
 // entry point are in include/fp8_moe_grouped.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "../../include/fp8_moe_grouped.h"
 #include "launch.hpp"
 
 using namespace fp8gmm;
+
+// Scratch of gmm_fp8_fwd_noalloc: the activation codes and row scales that
+// gmm_fp8_fwd keeps in the caller's workspace.  Every GPU the library runs on
+// holds its own copy until the process ends.  Host code never uses this name
+// as an address (on the host it is only a stand-in): the device address comes
+// from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[FP8GMM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -61,6 +70,27 @@ int fwd_common(const void* lhs, const uint8_t* codes, const float* scale, const 
 
 }  // namespace
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per device id
+
+// Device address of the current device's scratch (looked up on the first call
+// on each device; a race between two first calls stores the same address).
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8GMM_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FP8GMM_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FP8GMM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
@@ -68,6 +98,23 @@ int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const
                 size_t ws_bytes, int32_t* dev_status, void* stream) {
   return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, nullptr, dbg_codes, dbg_scale, ws, ws_bytes,
                     dev_status, stream, false);
+}
+
+int gmm_fp8_fwd_noalloc(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                        int64_t M, int64_t K, int64_t N, int32_t G, void* out, int32_t* dev_status, void* stream) {
+  if (!codes || !scale || !group_sizes) return FP8GMM_ERR_NULL;
+  int st = check_common(M, K, N, G);
+  if (st != FP8GMM_OK) return st;
+  if (M > 0 && (!lhs || !out)) return FP8GMM_ERR_NULL;
+  if (K > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
+  if (!aligned16(lhs) || !aligned16(codes) || !aligned16(scale) || !aligned16(out)) return FP8GMM_ERR_ALIGN;
+  if (fwd_ws(M, K) > FP8GMM_NOALLOC_SCRATCH_BYTES) return FP8GMM_ERR_SCRATCH;
+  if (M == 0) return FP8GMM_OK;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != FP8GMM_OK) return st;
+  return fwd_common(lhs, codes, scale, group_sizes, M, K, N, G, out, nullptr, nullptr, nullptr, ws,
+                    FP8GMM_NOALLOC_SCRATCH_BYTES, dev_status, stream, false);
 }
 
 int gmm_silu_fp8(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes, int64_t M,
@@ -394,6 +441,7 @@ const char* fp8gmm_status_string(int32_t status) {
     case FP8GMM_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case FP8GMM_ERR_WORKSPACE: return "workspace missing or too small";
     case FP8GMM_ERR_HIP: return "a HIP kernel launch failed";
+    case FP8GMM_ERR_SCRATCH: return "the input does not fit the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

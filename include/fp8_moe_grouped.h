@@ -51,6 +51,7 @@ extern "C" {
 #define FP8GMM_ERR_ALIGN (-4)       /* a base pointer is not 16-byte aligned */
 #define FP8GMM_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than fp8gmm_workspace_bytes */
 #define FP8GMM_ERR_HIP (-6)         /* a kernel launch failed */
+#define FP8GMM_ERR_SCRATCH (-7)     /* input larger than gmm_fp8_fwd_noalloc's fixed scratch */
 
 /* bits of *dev_status */
 #define FP8GMM_DEV_SUM_CLAMPED 1    /* sum(group_sizes) > M, clamped */
@@ -99,6 +100,27 @@ extern "C" {
 int gmm_fp8_fwd(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
                 int64_t M, int64_t K, int64_t N, int32_t G, void* out, uint8_t* dbg_codes, float* dbg_scale,
                 void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * gmm_fp8_fwd_noalloc -- gmm_fp8_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, with no workspace and no
+ * debug outputs.  The activation codes and row scales go to a fixed scratch
+ * array inside the library, FP8GMM_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the library's load until the process ends.  The call allocates and frees
+ * nothing.  It needs A256(M*K) + A256(4*M) <= FP8GMM_NOALLOC_SCRATCH_BYTES
+ * (A256: rounded up to a multiple of 256), else it returns FP8GMM_ERR_SCRATCH
+ * before any HIP call (e.g. up to 4096 rows at K = 7168).  The current
+ * device's scratch is used, so `stream` must belong to the current device.
+ * All calls on one GPU share that GPU's scratch: calls that may overlap on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller.  Nothing in the scratch needs clearing between calls (every value
+ * read is written earlier in the same call).  Other arguments and errors as
+ * gmm_fp8_fwd.
+ */
+#define FP8GMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+int gmm_fp8_fwd_noalloc(const void* lhs, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
+                        int64_t M, int64_t K, int64_t N, int32_t G, void* out, int32_t* dev_status, void* stream);
 
 /*
  * gmm_silu_fp8 -- gmm_fp8_fwd with a fused SwiGLU epilogue for wi ("MoE: native FP8 QAT for routed-expert GMMs"

@@ -39,6 +39,8 @@ def test_header_macros_match_binding():
     assert vals["FP8GMM_OP_FFN_FWD"] == G.OP_FFN_FWD and vals["FP8GMM_OP_FFN_BWD"] == G.OP_FFN_BWD
     assert vals["FP8GMM_OP_FWD_VARIANT"] == G.OP_FWD_VARIANT and vals["FP8GMM_ACC_BF16"] == G.ACC_BF16
     assert vals["FP8GMM_LHS_SCALE_BF16"] == G.LHS_SCALE_BF16 and vals["FP8GMM_RHS_SCALE_FIRST"] == G.RHS_SCALE_FIRST
+    assert vals["FP8GMM_ERR_SCRATCH"] == G.ERR_SCRATCH
+    assert "#define FP8GMM_NOALLOC_SCRATCH_BYTES (32u << 20)" in text and G.NOALLOC_SCRATCH_BYTES == 32 << 20
 
 
 P = 0x10000          # fake, 16-byte aligned "device" address; never dereferenced
@@ -171,7 +173,7 @@ def test_workspace_and_status_strings():
     L = _lib()
     assert L.fp8gmm_workspace_bytes(G.OP_FWD, 256, 100, 256, 4, 512) == 0      # rejected sizes
     assert L.fp8gmm_workspace_bytes(G.OP_SILU, 8192, 2048, 1536, 8, 512) >= 8192 * 2048
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert G.status_string(s) and G.status_string(s) != "unknown status"
     assert G.status_string(-99) == "unknown status"
 
@@ -191,3 +193,21 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("no oracle", ""), os.path.join(dirpath, f)
+
+
+def test_noalloc_validation():
+    """The allocation-free forward rejects bad arguments, and inputs larger
+    than its fixed scratch, on the host before any HIP call."""
+    L = _lib()
+    f = L.gmm_fp8_fwd_noalloc
+    args = lambda **kw: [kw.get("lhs", P), kw.get("codes", P), P, P, kw.get("M", 4096), kw.get("K", 7168),
+                         kw.get("N", 2048), 32, kw.get("out", P), None, None]
+    assert f(*args(lhs=None)) == G.ERR_NULL
+    assert f(*args(out=None)) == G.ERR_NULL
+    assert f(*args(M=-1)) == G.ERR_SHAPE
+    assert f(*args(K=100)) == G.ERR_UNSUPPORTED
+    assert f(*args(codes=BAD)) == G.ERR_ALIGN
+    # 4096 rows of K = 7168 fit the 32 MiB scratch (codes + row scales); 4682 rows do not
+    assert 4096 * 7168 + 4096 * 4 <= G.NOALLOC_SCRATCH_BYTES < 4682 * 7168
+    assert f(*args(M=4682)) == G.ERR_SCRATCH
+    assert f(*args(M=1 << 20, K=128)) == G.ERR_SCRATCH
