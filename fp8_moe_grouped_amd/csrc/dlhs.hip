@@ -420,6 +420,227 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   }
 }
 
+// ---------------------------------------------------------------- cached weight block
+//
+// When the whole contraction of a k-tile fits the LDS as bf16 (BN output
+// columns x N contraction values), the block decodes that weight block once
+// and reuses it for every row of its chunk of the expert: the MI355X form of
+// the single-K-tile cache ("MoE: native FP8 QAT for routed-expert GMMs",
+// Implementation: with one K tile the dequantized block stays in VMEM across
+// its m tiles; the conversation page's review thread on the cache).  The
+// weight block is the decoded bf16 of dequantize_fp8_codes; it never leaves
+// the chip.
+//
+// A block owns (a chunk of up to chunk_rows rows of one expert, BN output
+// columns).  Fill: every thread decodes 16-code groups of the block's BN
+// weight rows (exact decode, f32 product with the channel's scale, one bf16
+// rounding) into LDS, laid out per 64-value contraction stage as
+// [BN rows][64 bf16] with the ring's 16-byte swizzle.  After one barrier the
+// LDS is read-only: each wave takes row tasks of RW rows of the chunk in turn
+// and runs the whole contraction for them with all BN columns, streaming its
+// dout rows from global memory straight into registers, D stages ahead of the
+// MFMAs (a buffer range per task: rows past the expert's end are never read,
+// a stage past the contraction's end loads zeros without a memory access).
+// No ring, no barrier in the main loop, so the waves on a SIMD drift apart
+// and cover each other's load latency.
+//
+// Each lane holds, for MFMA half s of stage ks, the contraction values
+// 64 ks + 16 (lane / 16) + 8 s + 0..7 of its weight column and dout row, and
+// every accumulator sees the stages in order, half 0 before half 1: the
+// operand assignment and order of the ring kernel, so the result is bit for
+// bit the ring kernel's (and the bf16 arm's on dequantize_fp8_codes' output).
+//
+// Why only 128 columns and contractions up to 512: every wave reads its dout
+// rows once per k-tile, so a block of BN columns reads dout K / BN times.
+// Narrower blocks (to fit a longer contraction) multiply that traffic: 32
+// columns at a contraction of 2048 (the pages' microbenchmark wi dLHS) read
+// dout 128 times and ran 4x slower than the ring kernel, which reads it K/256
+// times and decodes each weight tile once per 256 rows.  A 128-column block
+// reads dout twice as often as the ring but decodes each weight element once
+// per chunk of up to 2048 rows.
+constexpr int kCacheMax = 128 * 1024;             // LDS bytes of the cached block
+
+template <int BN>
+struct CacheCfg {
+  static constexpr int RW = 64;                  // rows per wave task
+  static constexpr int FBK = RW / 16;            // 16-row fragments per task
+  static constexpr int NJ = BN / 16;             // 16-column fragments (every column of the block)
+  static constexpr int D = 1;                    // dout stages in flight ahead of the MFMAs
+  static_assert(kCacheMax + sizeof(int) * (3 * kMaxGroups + 1) <= 160 * 1024, "cache + expert table fit the LDS");
+};
+
+template <int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void gmm_dlhs_cached_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restrict__ codes,
+                            const float* __restrict__ wscale, const int* __restrict__ group_sizes, int G, int M,
+                            int K, int N, int chunk_rows, uint16_t* __restrict__ dlhs, int* status) {
+  using C = CacheCfg<BN>;
+  constexpr int FBK = C::FBK, NJ = C::NJ, RW = C::RW, D = C::D;
+  constexpr int kStageBytes = BN * kARow;        // one contraction stage of the block: [BN][64] bf16
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int nk = N / BKN;
+  int* t_start = reinterpret_cast<int*>(smem + nk * kStageBytes);
+  int* t_end = t_start + G;
+  int* t_pre = t_end + G;
+
+  build_group_table(group_sizes, G, M, chunk_rows, GroupTable{t_start, t_end, t_pre}, status);
+  __syncthreads();
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k_tiles = K / BN;
+  const int T = t_pre[G];
+  if ((int)blockIdx.x >= T * k_tiles) return;
+  // groups of kGroupM chunks walk the k-tiles, chunk fastest (one chunk's rows per XCD)
+  int ct, kt;
+  raster_tile<kGroupM>(blockIdx.x, T, k_tiles, ct, kt);
+  kt = __builtin_amdgcn_readfirstlane(kt);
+  const int g = __builtin_amdgcn_readfirstlane(find_group(t_pre, G, ct));
+  const int row0 = __builtin_amdgcn_readfirstlane(t_start[g] + (ct - t_pre[g]) * chunk_rows);
+  const int rows = __builtin_amdgcn_readfirstlane(min(chunk_rows, t_end[g] - row0));
+
+  // ---- fill: weight rows kt*BN .. kt*BN+BN-1 over the whole contraction, decoded once
+  {
+    const uint8_t* cg = codes + ((size_t)g * K + (size_t)kt * BN) * N;
+    const float* sg = wscale + (size_t)g * N;
+    const int nu = N >> 4;                        // 16-value groups per weight row
+    for (int t = tid; t < BN * nu; t += kThreads) {
+      const int c = t / nu, u = t - c * nu;
+      const v4i w = *reinterpret_cast<const v4i*>(cg + (size_t)c * N + 16 * u);
+      const v4f* sp = reinterpret_cast<const v4f*>(sg + 16 * u);
+      v4i o[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint32_t word = (uint32_t)w[2 * h + p];
+          const v4f sc = sp[2 * h + p];
+          const v2f lo = dec_e4m3x2<false>(word), hi = dec_e4m3x2<true>(word);
+          o[h][2 * p] = (int)pack_bf16x2(lo[0] * sc[0], lo[1] * sc[1]);
+          o[h][2 * p + 1] = (int)pack_bf16x2(hi[0] * sc[2], hi[1] * sc[3]);
+        }
+      uint8_t* st = smem + (u >> 2) * kStageBytes;   // stage of these 16 values
+      const int ch = (u & 3) * 2;                    // their first 8-value chunk in the stage
+      *reinterpret_cast<v4i*>(st + a_swz(c, ch)) = o[0];
+      *reinterpret_cast<v4i*>(st + a_swz(c, ch + 1)) = o[1];
+    }
+  }
+  __syncthreads();
+
+  // ---- row tasks: wave w takes tasks w, w + 8, ... of the chunk
+  const int q = lane >> 4;
+  int w_rd[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) w_rd[s] = a_swz(lane & 15, 2 * q + s);   // + j * 2048 (+ ks * kStageBytes)
+  const int ntask = (rows + RW - 1) / RW;
+  // Lanes l and l^16 hold the same row, columns 4q..4q+3 and 4q+4..4q+7 (q
+  // even) of two adjacent 16-column fragments: trading one 8-byte group makes
+  // every store 16 bytes (as in the ring kernel's epilogue).
+  auto store_pair = [&](uint16_t* p, const v2i& x0, const v2i& x1) __attribute__((always_inline)) {
+    const bool ev = (q & 1) == 0;
+    const v2i sv = ev ? x1 : x0;
+    const int r0 = __shfl_xor(sv[0], 16), r1 = __shfl_xor(sv[1], 16);
+    const v4i v = ev ? (v4i){x0[0], x0[1], r0, r1} : (v4i){r0, r1, x1[0], x1[1]};
+    *reinterpret_cast<v4i*>(p + (ev ? 4 * q : 16 + 4 * (q - 1))) = v;
+  };
+  for (int task = wave; task < ntask; task += kThreads / 64) {
+    const int tr0 = row0 + task * RW;
+    const int trows = min(RW, rows - task * RW);
+    // this task's rows of dout; a load at or past the range's end returns zeros
+    const BufRsrc rd = make_rsrc(dout + (size_t)tr0 * N, (uint32_t)trows * (uint32_t)N * 2u);
+    uint32_t voff[FBK];
+#pragma unroll
+    for (int f = 0; f < FBK; ++f)
+      voff[f] = (uint32_t)min(16 * f + (lane & 15), trows - 1) * (uint32_t)N * 2u + 32u * (uint32_t)q;
+    const uint32_t kPast = 1u << 31;             // a stage offset past the range: no memory access
+    auto load = [&](v4i (&b)[FBK][2], int ks) __attribute__((always_inline)) {
+      const uint32_t so = ks < nk ? (uint32_t)ks * (uint32_t)kARow : kPast;
+#pragma unroll
+      for (int f = 0; f < FBK; ++f)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          b[f][s] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rd, voff[f] + 16u * s, so, 0));
+    };
+    v4f acc[FBK][NJ];
+#pragma unroll
+    for (int f = 0; f < FBK; ++f)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const v4i (&b)[FBK][2], int ks) __attribute__((always_inline)) {
+      const uint8_t* st = smem + ks * kStageBytes;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const v4i w0 = *reinterpret_cast<const v4i*>(st + j * 2048 + w_rd[0]);
+        const v4i w1 = *reinterpret_cast<const v4i*>(st + j * 2048 + w_rd[1]);
+#pragma unroll
+        for (int f = 0; f < FBK; ++f) acc[f][j] = mfma_bf16_16x16x32(as_bf(w0), as_bf(b[f][0]), acc[f][j]);
+#pragma unroll
+        for (int f = 0; f < FBK; ++f) acc[f][j] = mfma_bf16_16x16x32(as_bf(w1), as_bf(b[f][1]), acc[f][j]);
+      }
+    };
+    // Two register buffers, unrolled so that each is named at compile time.
+    // The loop body has no branch (a load whose only use sits behind a branch
+    // gets sunk into it, next to its wait); a load past the contraction's end
+    // loads nothing, and the odd last stage runs after the loop.  The fences
+    // keep each load ahead of the MFMAs it overlaps.
+    static_assert(D == 1, "one stage of dout in flight");
+    v4i b0[FBK][2], b1[FBK][2];
+    load(b0, 0);
+    sched_fence();
+    int ks = 0;
+    for (; ks + 1 < nk; ks += 2) {
+      load(b1, ks + 1);
+      sched_fence();
+      compute(b0, ks);
+      sched_fence();
+      load(b0, ks + 2);
+      sched_fence();
+      compute(b1, ks + 1);
+      sched_fence();
+    }
+    if (ks < nk) compute(b0, ks);
+    // ---- epilogue: lane owns row tr0 + 16 f + lane%16, columns kt*BN + 16 j + 4 q + 0..3
+#pragma unroll
+    for (int f = 0; f < FBK; ++f) {
+      const int ml = 16 * f + (lane & 15);
+      if (ml < trows) {
+        uint16_t* orow = dlhs + (size_t)(tr0 + ml) * K + (size_t)kt * BN;
+        v2i pk[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          pk[j][0] = (int)pack_bf16x2(acc[f][j][0], acc[f][j][1]);
+          pk[j][1] = (int)pack_bf16x2(acc[f][j][2], acc[f][j][3]);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; j += 2) store_pair(orow + j * 16, pk[j], pk[j + 1]);
+      }
+    }
+  }
+}
+
+// The cached block's column width for contraction N (0: the ring kernel).
+int cached_bn(int N) { return 2 * 128 * N <= kCacheMax ? 128 : 0; }
+
+template <int BN>
+hipError_t launch_dlhs_cached(const uint16_t* dout, const uint8_t* codes, const float* scale, const int* group_sizes,
+                              int G, int M, int K, int N, uint16_t* dlhs, int* status, hipStream_t stream) {
+  // rows per block: the largest of 2048 / 1024 / 512 / 256 that still gives two blocks per CU
+  const long long k_tiles = K / BN;
+  const long long want = 2LL * device_cu_count();
+  int chunk = 256;
+  for (int c : {2048, 1024, 512}) {
+    if (((long long)M / c + G) * k_tiles >= want) {
+      chunk = c;
+      break;
+    }
+  }
+  const long long grid = ((long long)(M + chunk - 1) / chunk + G) * k_tiles;
+  const size_t lds = (size_t)2 * BN * N + sizeof(int) * (3 * (size_t)G + 1);
+  hipLaunchKernelGGL((gmm_dlhs_cached_kernel<BN>), dim3((unsigned)grid), dim3(kThreads), lds, stream, dout, codes,
+                     scale, group_sizes, G, M, K, N, chunk, dlhs, status);
+  return hipGetLastError();
+}
+
 template <bool FROM_CODES, bool DSWIGLU, int BM>
 hipError_t launch_dlhs_bm(const uint16_t* dout, const uint8_t* codes, const float* scale, const uint16_t* wbf16,
                           const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact, uint16_t* dlhs,
@@ -446,6 +667,11 @@ hipError_t launch_dlhs_impl(const uint16_t* dout, const uint8_t* codes, const fl
                             const int* group_sizes, int G, int M, int K, int N, const uint16_t* preact,
                             uint16_t* dlhs, int* status, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  // the whole contraction of a k-tile fits the LDS: decode each weight block once per chunk of rows
+  if constexpr (FROM_CODES && !DSWIGLU) {
+    if (cached_bn(N) == 128)
+      return launch_dlhs_cached<128>(dout, codes, scale, group_sizes, G, M, K, N, dlhs, status, stream);
+  }
   // skinny groups (at most 64 rows per expert on average): 64-row tiles
   if ((long long)M <= 64LL * G)
     return launch_dlhs_bm<FROM_CODES, DSWIGLU, 64>(dout, codes, scale, wbf16, group_sizes, G, M, K, N, preact, dlhs,

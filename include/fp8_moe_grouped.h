@@ -188,7 +188,11 @@ int gmm_fp8_fwd_variant(const void* lhs, const uint8_t* codes, const float* scal
  *   w[g,k,n]    = bf16( f32(codes[g,k,n] * scale[g,n]) )   (as dequantize_fp8_codes)
  *   dlhs[r,k]   = bf16( sum_n dout[r,n] * w[g,k,n] )        f32 accumulation
  * dout bf16 [M, N]; dlhs bf16 [M, K] (rows >= sum(group_sizes) not written).
- * The call needs no workspace (ws may be NULL).
+ * When the contraction N is at most 512, each 128-column block of w is
+ * decoded once and kept on chip for a chunk of up to 2048 rows of its expert
+ * (same Implementation section: with one K tile the dequantized block is
+ * cached across its m tiles); otherwise each tile is decoded as it is used.
+ * Both give the same bits.  The call needs no workspace (ws may be NULL).
  */
 int gmm_dlhs_fp8(const void* dout, const uint8_t* codes, const float* scale, const int32_t* group_sizes,
                  int64_t M, int64_t K, int64_t N, int32_t G, void* dlhs, void* ws, size_t ws_bytes,

@@ -134,6 +134,30 @@ def test_dlhs_edges_and_stale_tail():
     assert st == 3
 
 
+@pytest.mark.parametrize("N,K", [(128, 256), (256, 128), (512, 384), (640, 256)])
+def test_dlhs_cached_block_boundaries(N, K):
+    """Contractions on both sides of the cached-block limit: up to 512 a block
+    decodes its 128 weight columns over the whole contraction once and keeps
+    them in LDS for all its rows, beyond that the ring kernel decodes per
+    stage.  The
+    experts include one spanning several 2048-row chunks, an empty one, a
+    single-row one and a ragged tail before a garbage tail; every row against
+    the oracle and the whole result bit for bit against the bf16 main loop on
+    dequantize_fp8_codes' output."""
+    r = np.random.default_rng(N + K)
+    G_, M = 5, 5200
+    gs = [2600, 0, 1, 1700, 800]                  # 5101 valid rows, 99 stale
+    codes = np.empty((G_, K, N), np.uint8)
+    scale = np.empty((G_, N), np.float32)
+    for g in range(G_):
+        codes[g], scale[g] = W.weight_codes(r.standard_normal((K, N)).astype(np.float32) * 0.02)
+    dout = W.to_bf16_bits(r.standard_normal((M, N)).astype(np.float32) * 1e-3)
+    W.fill_garbage(dout, sum(gs))
+    err, st = check_dlhs(dict(codes=codes, scale=scale, dout=dout), gs=gs)
+    assert st == 0
+    print(f"dlhs N={N} K={K}: normwise {err[0]:.2e} ratio {err[1]:.3f}")
+
+
 @pytest.mark.parametrize("K", [2048, 1152])
 def test_dlhs_skinny_groups(K):
     """Skinny groups (a buffer of at most 64 rows per expert on average):
