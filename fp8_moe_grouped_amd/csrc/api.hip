@@ -236,7 +236,7 @@ int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, in
   if (st != FP8GMM_OK) return st;
   if (M > 0 && (!lhs || !dout)) return FP8GMM_ERR_NULL;
   if (grad_dtype != FP8GMM_E4M3 && grad_dtype != FP8GMM_E5M2) return FP8GMM_ERR_UNSUPPORTED;
-  if (tile_m != 512 || K % 256 != 0) return FP8GMM_ERR_UNSUPPORTED;
+  if (tile_m != 512) return FP8GMM_ERR_UNSUPPORTED;
   if (!aligned16(lhs) || !aligned16(dout) || !aligned16(drhs) || (dbg_sL && !aligned16(dbg_sL)) ||
       (dbg_sD && !aligned16(dbg_sD)))
     return FP8GMM_ERR_ALIGN;
@@ -274,7 +274,7 @@ int tgmm_dense_quant(const void* lhs, const void* dout, const int32_t* group_siz
   if (st != FP8GMM_OK) return st;
   if (M > 0 && (!lhs || !dout)) return FP8GMM_ERR_NULL;
   if (grad_dtype != FP8GMM_E4M3 && grad_dtype != FP8GMM_E5M2) return FP8GMM_ERR_UNSUPPORTED;
-  if (K % 256 != 0 || K > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
+  if (K > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
   if (!aligned16(lhs) || !aligned16(dout) || !aligned16(drhs) || (dbg_col_scale && !aligned16(dbg_col_scale)))
     return FP8GMM_ERR_ALIGN;
   const size_t need = tgmm_dense_workspace_bytes(M, K, N, G);
@@ -335,7 +335,7 @@ static int check_ffn(int64_t M, int64_t H, int64_t I, int32_t G) {
   if (st != FP8GMM_OK) return st;
   st = check_common(M, I, H, G);
   if (st != FP8GMM_OK) return st;
-  if (H % 256 != 0 || I % 256 != 0 || H > kMaxK || I > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
+  if (H > kMaxK || I > kMaxK) return FP8GMM_ERR_UNSUPPORTED;
   return FP8GMM_OK;
 }
 
@@ -418,9 +418,9 @@ size_t fp8gmm_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32
     case FP8GMM_OP_SILU:
       return fwd_ws(M, K);
     case FP8GMM_OP_TGMM:
-      return (tile_m == 512 && K % 256 == 0) ? tgmm_workspace_bytes(M, K, N, G) : 0;
+      return tile_m == 512 ? tgmm_workspace_bytes(M, K, N, G) : 0;
     case FP8GMM_OP_TGMM_DENSE:
-      return (K % 256 == 0 && K <= kMaxK) ? tgmm_dense_workspace_bytes(M, K, N, G) : 0;
+      return K <= kMaxK ? tgmm_dense_workspace_bytes(M, K, N, G) : 0;
     case FP8GMM_OP_FWD_VARIANT:
       return (tile_m == 0 || tile_m == 512) ? variant_ws(M, K, tile_m) : 0;
     case FP8GMM_OP_FFN_FWD:

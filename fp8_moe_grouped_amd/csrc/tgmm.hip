@@ -16,11 +16,12 @@
 //     LDS), writes the scales and stores the 8-bit codes row-major into the
 //     pair's slab of the workspace ([512 rows][columns], rows past the pair's
 //     end up to the next multiple of 32 hold zero codes).
-//  2. gemm: persistent, one block per CU, walking its share of the work
-//     items (expert, 256-row k tile, 128-column n tile); an item covers the
-//     expert's pairs 128 rows at a time.  The code chunks of both operands
-//     are copied HBM -> LDS by buffer loads with an LDS destination through a
-//     three-stage ring that runs across pairs and items, so copy latency is
+//  2. gemm: persistent, walking each block's share of the work items
+//     (expert, k tile of 256 rows -- 128 when K is not a multiple of 256 --,
+//     128-column n tile); an item covers the expert's pairs 128 (64) rows at
+//     a time.  The code chunks of both operands are copied HBM -> LDS by
+//     buffer loads with an LDS destination through a three- (four-) stage
+//     ring that runs across pairs and items, so copy latency is
 //     paid once per block rather than once per tile; a pair's last stage
 //     reads zeros past its padded rows (the copy's buffer range ends there).  The contraction runs
 //     over rows, which is the slow axis of both tiles, so the MFMA operands
@@ -29,14 +30,15 @@
 //     e4m3/e5m2 value is exact in bf16 and products are exact in f32) keeps
 //     f32 accuracy; gfx950's FP8 MFMA adds its 128 products in a narrower
 //     adder, about 2^-16 of the absolute sum, too coarse for an f32 gradient.
-//     Eight waves (two per SIMD) own 64 x 64 of the tile each; a per-pair
+//     Eight (four) waves own 64 x 64 of the tile each, two per SIMD (the
+//     128-row form runs two blocks per CU); a per-pair
 //     partial accumulator is rescaled by sL x sD and added to the total at
 //     the pair's end.  The pair's scales travel with each stage's copy into
 //     the ring, so the rescale reads LDS and never waits on a global load
 //     (such a wait also waits for every copy in flight).  A pair's last
 //     stage runs only the 32-row sub-steps its rows cover.  Experts without
 //     rows get zeros.  The f32 output is written with 16-byte streaming
-//     stores of whole cache lines, which drain while the next item computes.
+//     stores of whole cache lines.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,7 +50,6 @@ namespace {
 constexpr int kTileM = 512;       // rows per gm-tile (the only supported value)
 constexpr int kPrepCols = 64;     // columns per prep block
 constexpr int kSub = 32;          // contraction rows per MFMA sub-step (slabs are padded to this)
-constexpr int kChunk = 128;       // contraction rows per GEMM stage (1 to 4 sub-steps)
 constexpr int kThreads = 256;
 
 // Pair table from group_sizes, built by wave 0 into LDS: expert g owns rows
@@ -364,24 +365,47 @@ __global__ __launch_bounds__(kThreads) void dense_gather_kernel(const uint8_t* _
 
 // ------------------------------------------------------------------ gemm
 
-constexpr int BMK = 256;                        // drhs rows (k) per block
-constexpr int BNN = 128;                        // drhs columns (n) per block
-constexpr int kGThreads = 512;                  // 8 waves: 4 along k x 2 along n, 64 x 64 each
-constexpr int kAStage = kChunk * BMK;           // qL codes [128 rows][256 k]
-constexpr int kBStage = kChunk * BNN;           // qD codes [128 rows][128 n]
-constexpr int kSStage = 4 * (BMK + BNN);        // the stage's pair's scales: sL [256 k], sD [128 n]
-constexpr int kStageG = kAStage + kBStage + kSStage;
-constexpr int kStagesG = 3;
-constexpr int kLdsG = kStagesG * kStageG;
-static_assert(kLdsG + sizeof(int) * 2 * (kMaxGroups + 1) <= 160 * 1024, "ring + expert table fit the LDS");
-constexpr int kALoadsG = kAStage / (8 * 1024);  // 1 KB wave-wide loads per wave per stage
-constexpr int kBLoadsG = kBStage / (8 * 1024);
-constexpr int kLoadsG = kALoadsG + kBLoadsG + 1;   // + one 256-byte scale slice per wave
-
-// 16-byte chunk swizzles: the 16 lanes of a transposing read touch 8
-// consecutive rows at one chunk, and two such groups are served together.
-__device__ __forceinline__ int l_slot(int row, int chunk) { return row * BMK + ((chunk ^ (row & 15)) << 4); }
-__device__ __forceinline__ int d_slot(int row, int chunk) { return row * BNN + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// Two geometries of the GEMM, by the width of the k tile (drhs rows per work
+// item), BMK = 256 when K allows it, else 128:
+//   256: 8 waves (4 along k x 2 along n, 64 x 64 each), 128-row stages in a
+//        three-slot ring (144 KB), one block per CU;
+//   128: 4 waves (2 x 2), 64-row stages in a four-slot ring (68 KB), two
+//        blocks per CU.
+// Measured on the dropless 7168 x 2048 gradient (K = 7168 takes the 256 form):
+// the GEMM ran 911 us with 256-row k tiles against 939 us with 128-row tiles
+// and two blocks per CU (its MFMAs busy 28 % of the time, waves stalled on
+// the vector-memory counter 45 %: the copies' latency, not bandwidth, bounds
+// both forms).
+template <int BMK_>
+struct TgCfg {
+  static constexpr int BMK = BMK_;                 // drhs rows (k) per work item
+  static constexpr int BNN = 128;                  // drhs columns (n) per work item
+  static constexpr bool kWide = BMK_ == 256;
+  static constexpr int kThreads = kWide ? 512 : 256;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kChunk = kWide ? 128 : 64;  // contraction rows per stage (sub-steps of kSub)
+  static constexpr int kStages = kWide ? 3 : 4;
+  static constexpr int kBlocksPerCU = kWide ? 1 : 2;
+  static constexpr int kAStage = kChunk * BMK;     // qL codes [kChunk rows][BMK k]
+  static constexpr int kBStage = kChunk * BNN;     // qD codes [kChunk rows][128 n]
+  static constexpr int kSStage = 4 * (BMK + BNN);  // the stage's pair's scales: sL [BMK k], sD [128 n]
+  static constexpr int kStage = kAStage + kBStage + kSStage;
+  static constexpr int kLds = kStages * kStage;
+  static constexpr int kALoads = kAStage / (kWaves * 1024);   // 1 KB wave-wide loads per wave per stage
+  static constexpr int kBLoads = kBStage / (kWaves * 1024);
+  static constexpr int kLoads = kALoads + kBLoads + 1;        // + one 256-byte scale slice per wave
+  static constexpr int kARows = 1024 / BMK;                   // qL rows per 1 KB load
+  static constexpr int kAChunks = BMK / 16;                   // 16-byte chunks per qL row
+  static constexpr int kSlicesL = BMK / 64;                   // 256-byte sL slices per stage
+  static_assert(kBlocksPerCU * (kLds + sizeof(int) * 2 * (kMaxGroups + 1)) <= 160 * 1024,
+                "the rings and expert tables of a CU's blocks fit the LDS");
+  static_assert(kLoads * (kStages - 1) < 64, "outstanding copies fit vmcnt");
+  // 16-byte chunk swizzles: the 16 lanes of a transposing read touch 8
+  // consecutive rows at one chunk, and two such groups are served together.
+  static __device__ __forceinline__ int a_key(int row) { return kWide ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ int l_slot(int row, int chunk) { return row * BMK + ((chunk ^ a_key(row)) << 4); }
+  static __device__ __forceinline__ int d_slot(int row, int chunk) { return row * BNN + ((chunk ^ ((row >> 1) & 7)) << 4); }
+};
 
 // 8 codes (8 consecutive rows of one column) -> 8 bf16, exactly.
 template <bool E5M2>
@@ -403,18 +427,19 @@ __device__ __forceinline__ v4i widen8(const v2i& c) {
   return o;
 }
 
-// Where a wave's share of a stage's copy goes: operand codes (kALoadsG +
-// kBLoadsG 1 KB loads) and one 256-byte slice of the pair's scales (waves 0-3
-// the four sL quarters, waves 4-5 the two sD halves, waves 6-7 the sD halves
-// again, landing on the same bytes with the same values), so every wave
-// issues the same number of copies per stage.
+// Where a wave's share of a stage's copy goes: operand codes (kALoads +
+// kBLoads 1 KB loads) and one 256-byte slice of the pair's scales (the first
+// kSlicesL waves the sL slices, the next two the sD halves, any further waves
+// the sD halves again, landing on the same bytes with the same values), so
+// every wave issues the same number of copies per stage.
+template <class C>
 struct StageCopy {
   BufRsrc ra, rb, rs;
-  uint32_t va[kALoadsG], vb[kBLoadsG];   // per-lane offsets (held by value: no array in memory)
+  uint32_t va[C::kALoads], vb[C::kBLoads];   // per-lane offsets (held by value: no array in memory)
   uint32_t soa, sob, vs, s_lds;
 };
 
-// One 128-row stage: optionally start the copy of a later stage into `wr`,
+// One stage of kChunk rows: optionally start the copy of a later stage into `wr`,
 // then read this stage's operands from `rd` and run its first `nsub` (of NS)
 // 32-row sub-steps of 16 MFMAs per wave.  On a pair's last stage (`last`)
 // the partial is rescaled by the pair's scales, read from this stage's slot,
@@ -422,17 +447,17 @@ struct StageCopy {
 // `wr` and `rd` are distinct ring slots; marking them __restrict__ lets the
 // compiler see that the reads cannot depend on the copy just issued, so it
 // adds no wait for it (the kernel's own wait + barrier order the ring).
-template <bool GRAD_E5M2, int NS>
+template <bool GRAD_E5M2, class C, int NS = C::kChunk / kSub>
 __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8_t* __restrict__ rd, bool copy,
-                                           const StageCopy& cp, int wave, const int* a_rd, const int* b_rd,
+                                           const StageCopy<C>& cp, int wave, const int* a_rd, const int* b_rd,
                                            int nsub, bool last, int sl_rd, int sd_rd, v4f (&part)[4][4],
                                            v4f (&tot)[4][4]) {
   if (copy) {
 #pragma unroll
-    for (int j = 0; j < kALoadsG; ++j) dma16(cp.ra, wr + (kALoadsG * wave + j) * 1024, cp.va[j], cp.soa);
+    for (int j = 0; j < C::kALoads; ++j) dma16(cp.ra, wr + (C::kALoads * wave + j) * 1024, cp.va[j], cp.soa);
 #pragma unroll
-    for (int j = 0; j < kBLoadsG; ++j) dma16(cp.rb, wr + kAStage + (kBLoadsG * wave + j) * 1024, cp.vb[j], cp.sob);
-    dma4(cp.rs, wr + kAStage + kBStage + cp.s_lds, cp.vs, 0);
+    for (int j = 0; j < C::kBLoads; ++j) dma16(cp.rb, wr + C::kAStage + (C::kBLoads * wave + j) * 1024, cp.vb[j], cp.sob);
+    dma4(cp.rs, wr + C::kAStage + C::kBStage + cp.s_lds, cp.vs, 0);
   }
   // Sub-steps are software-pipelined: the codes of sub-step s+1 are read
   // before sub-step s's MFMAs and widened after them.
@@ -447,9 +472,9 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
     v2i cb[4], ca[4];
     if (s + 1 < NS) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) cb[j] = lds_read_tr8(rd + b_rd[j] + (s + 1) * 32 * BNN);
+      for (int j = 0; j < 4; ++j) cb[j] = lds_read_tr8(rd + b_rd[j] + (s + 1) * 32 * C::BNN);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) ca[f] = lds_read_tr8(rd + a_rd[f] + (s + 1) * 32 * BMK);
+      for (int f = 0; f < 4; ++f) ca[f] = lds_read_tr8(rd + a_rd[f] + (s + 1) * 32 * C::BMK);
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f)
@@ -482,14 +507,19 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
   }
 }
 
-template <bool GRAD_E5M2>
-__global__ __attribute__((amdgpu_flat_work_group_size(kGThreads, kGThreads), amdgpu_waves_per_eu(2, 2)))
+template <bool GRAD_E5M2, int BMK_>
+__global__ __attribute__((amdgpu_flat_work_group_size(TgCfg<BMK_>::kThreads, TgCfg<BMK_>::kThreads),
+                          amdgpu_waves_per_eu(2, 2)))
 void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict__ qd,
                       const float* __restrict__ sl, const float* __restrict__ sd,
                       const int* __restrict__ group_sizes, int G, int M, int K, int N,
                       float* __restrict__ drhs) {
+  using C = TgCfg<BMK_>;
+  constexpr int BMK = C::BMK, BNN = C::BNN, kChunk = C::kChunk, kStagesG = C::kStages, kStageG = C::kStage;
+  constexpr int kAStage = C::kAStage, kBStage = C::kBStage, kALoadsG = C::kALoads, kBLoadsG = C::kBLoads;
+  constexpr int kLoadsG = C::kLoads;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int* g_start = reinterpret_cast<int*>(smem + kLdsG);
+  int* g_start = reinterpret_cast<int*>(smem + C::kLds);
   int* p_base = g_start + G + 1;
   PairTable pt{g_start, p_base};
   build_pair_table(group_sizes, G, M, pt, nullptr);
@@ -516,8 +546,8 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   uint32_t va[kALoadsG], vb[kBLoadsG];
 #pragma unroll
   for (int j = 0; j < kALoadsG; ++j) {
-    const int row = (kALoadsG * wave + j) * 4 + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
+    const int row = (kALoadsG * wave + j) * C::kARows + lane / C::kAChunks;
+    const int ch = (lane % C::kAChunks) ^ C::a_key(row);
     va[j] = (uint32_t)row * (uint32_t)K + (uint32_t)(ch * 16);
   }
 #pragma unroll
@@ -530,9 +560,9 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   const int rbase = (lane >> 4) * 8 + (Lg >> 1);      // + 32 * s
   int a_rd[4], b_rd[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) a_rd[f] = l_slot(rbase, wk * 4 + f) + 8 * (Lg & 1);
+  for (int f = 0; f < 4; ++f) a_rd[f] = C::l_slot(rbase, wk * 4 + f) + 8 * (Lg & 1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b_rd[j] = kAStage + d_slot(rbase, wn * 4 + j) + 8 * (Lg & 1);
+  for (int j = 0; j < 4; ++j) b_rd[j] = kAStage + C::d_slot(rbase, wn * 4 + j) + 8 * (Lg & 1);
   // the rescale's scales in a stage slot: sL[wk*64 + f*16 + lane%16], sD[wn*64 + j*16 + 4*(lane/16) + 0..3]
   const int sl_rd = kAStage + kBStage + 4 * (wk * 64 + Lg);
   const int sd_rd = kAStage + kBStage + 4 * BMK + 4 * (wn * 64 + 4 * (lane >> 4));
@@ -573,8 +603,8 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
     for (int j = 0; j < kBLoadsG; ++j) vb_i[j] = vb[j] + (uint32_t)int_ * BNN;
   };
   // this wave's slice of the pair's scales (see StageCopy)
-  const bool s_is_l = wave < 4;
-  const int s_part = s_is_l ? wave : (wave - 4) & 1;
+  const bool s_is_l = wave < C::kSlicesL;
+  const int s_part = s_is_l ? wave : (wave - C::kSlicesL) & 1;
   const uint32_t s_lds = (s_is_l ? 0u : 4u * BMK) + 256u * (uint32_t)s_part;
   // The slice's source is written without a select between the copy-side
   // tile indices (the optimizer turns such a select into one between their
@@ -584,7 +614,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   const int s_mul_k = __builtin_amdgcn_readfirstlane(s_is_l ? BMK : 0);
   const int s_mul_n = __builtin_amdgcn_readfirstlane(s_is_l ? 0 : BNN);
   auto stage_copy = [&]() {
-    StageCopy cp;
+    StageCopy<C> cp;
     cp.ra = copy_rsrc_a();
     cp.rb = copy_rsrc_b();
     cp.rs = make_rsrc(s_base + (size_t)ip * s_stride, 4u * (uint32_t)s_stride);
@@ -614,7 +644,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   };
   auto issue = [&]() {          // prologue copies (nothing is read yet)
     uint8_t* St = smem + (tI % kStagesG) * kStageG;
-    const StageCopy cp = stage_copy();
+    const StageCopy<C> cp = stage_copy();
 #pragma unroll
     for (int j = 0; j < kALoadsG; ++j) dma16(cp.ra, St + (kALoadsG * wave + j) * 1024, cp.va[j], cp.soa);
 #pragma unroll
@@ -652,15 +682,16 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
         // it may still be in flight; other loads and stores only make the
         // wait stricter); stage tC-1's buffer is free for the next copy
         const int pending = tI - 1 - tC;
-        static_assert(kStagesG == 3, "one wait per possible count below");
-        if (pending >= 1) wait_vmem_lds<kLoadsG>();
+        static_assert(kStagesG == 3 || kStagesG == 4, "one wait per possible count below");
+        if (kStagesG == 4 && pending >= 2) wait_vmem_lds<(kStagesG == 4 ? 2 : 1) * kLoadsG>();
+        else if (pending >= 1) wait_vmem_lds<kLoadsG>();
         else wait_vmem_lds<0>();
         barrier_only();
         const bool copy = ii < total;
         uint8_t* wr = smem + (tI % kStagesG) * kStageG;
         const uint8_t* rd = smem + (tC % kStagesG) * kStageG;
         const int nsub = min(kChunk, rpad - c * kChunk) / kSub;
-        tgmm_stage<GRAD_E5M2, kChunk / kSub>(wr, rd, copy, stage_copy(), wave, a_rd, b_rd, nsub, c == nc - 1, sl_rd,
+        tgmm_stage<GRAD_E5M2, C>(wr, rd, copy, stage_copy(), wave, a_rd, b_rd, nsub, c == nc - 1, sl_rd,
                                              sd_rd, part, tot);
         if (copy) advance();
       }
@@ -712,19 +743,30 @@ size_t tgmm_workspace_bytes(long long M, long long K, long long N, int G) {
 namespace {
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
+template <int BMK>
+hipError_t launch_tgmm_gemm_bmk(const uint8_t* ql, const uint8_t* qd, const float* sl, const float* sd,
+                                const int* group_sizes, int G, int M, int K, int N, bool grad_e5m2, float* drhs,
+                                hipStream_t stream) {
+  using C = TgCfg<BMK>;
+  const size_t lds = C::kLds + sizeof(int) * 2 * ((size_t)G + 1);
+  const long long items = (long long)G * (K / BMK) * (N / C::BNN);
+  // persistent: as many blocks as stay resident at once
+  const dim3 grid((unsigned)std::min<long long>(items, (long long)C::kBlocksPerCU * device_cu_count()));
+  if (grad_e5m2)
+    hipLaunchKernelGGL((tgmm_gemm_kernel<true, BMK>), grid, dim3(C::kThreads), lds, stream, ql, qd, sl, sd,
+                       group_sizes, G, M, K, N, drhs);
+  else
+    hipLaunchKernelGGL((tgmm_gemm_kernel<false, BMK>), grid, dim3(C::kThreads), lds, stream, ql, qd, sl, sd,
+                       group_sizes, G, M, K, N, drhs);
+  return hipGetLastError();
+}
+
 hipError_t launch_tgmm_gemm(const uint8_t* ql, const uint8_t* qd, const float* sl, const float* sd,
                             const int* group_sizes, int G, int M, int K, int N, bool grad_e5m2, float* drhs,
                             hipStream_t stream) {
-  const size_t lds = kLdsG + sizeof(int) * 2 * ((size_t)G + 1);
-  const long long items = (long long)G * (K / BMK) * (N / BNN);
-  const dim3 grid((unsigned)std::min<long long>(items, device_cu_count()));   // one resident block per CU
-  if (grad_e5m2)
-    hipLaunchKernelGGL(tgmm_gemm_kernel<true>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G, M,
-                       K, N, drhs);
-  else
-    hipLaunchKernelGGL(tgmm_gemm_kernel<false>, grid, dim3(kGThreads), lds, stream, ql, qd, sl, sd, group_sizes, G,
-                       M, K, N, drhs);
-  return hipGetLastError();
+  if (K % 256 == 0)
+    return launch_tgmm_gemm_bmk<256>(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
+  return launch_tgmm_gemm_bmk<128>(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
 }
 }  // namespace
 

@@ -229,7 +229,7 @@ int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, 
  *   drhs[g,k,n] = f32( sum_t sL[k] sD[n] sum_{r in T} e4m3(lhs[r,k]/sL[k]) * grad(dout[r,n]/sD[n]) )
  * Experts without rows get exact zeros.  drhs f32 [G, K, N] is written fully.
  * lhs bf16 [M, K]; dout bf16 [M, N]; grad_dtype FP8GMM_E4M3 or FP8GMM_E5M2;
- * tile_m must be 512 and K a multiple of 256.  dbg_sL f32 [Tn, K] / dbg_sD f32 [Tn, N] (or NULL)
+ * tile_m must be 512 (K and N multiples of 128, as everywhere).  dbg_sL f32 [Tn, K] / dbg_sD f32 [Tn, N] (or NULL)
  * receive the scales of the Tn non-empty (expert, tile) pairs in (expert,
  * tile) order; Tn <= ceil(M/tile_m) + G - 1.
  * ws: fp8gmm_workspace_bytes(FP8GMM_OP_TGMM, M, K, N, G, 512) bytes.  After

@@ -90,8 +90,8 @@ def test_dswiglu_and_ffn_validation():
                                          kw.get("I", 256), 2, P, kw.get("pre", P), P, kw.get("ws", P),
                                          kw.get("wsb", 1 << 30), None, None)
     assert fwd(x=None) == G.ERR_NULL
-    assert fwd(H=384) == G.ERR_UNSUPPORTED               # tgmm needs multiples of 256
-    assert fwd(I=128) == G.ERR_UNSUPPORTED
+    assert fwd(H=192) == G.ERR_UNSUPPORTED               # every size a multiple of 128
+    assert fwd(I=64) == G.ERR_UNSUPPORTED
     assert fwd(pre=BAD) == G.ERR_ALIGN
     assert fwd(ws=None) == G.ERR_WORKSPACE
     need = L.fp8gmm_workspace_bytes(G.OP_FFN_FWD, 64, 512, 256, 2, 0)
@@ -136,7 +136,7 @@ def test_dense_validation():
     assert dn(lhs=None) == G.ERR_NULL
     assert dn(drhs=None) == G.ERR_NULL
     assert dn(gd=5) == G.ERR_UNSUPPORTED
-    assert dn(K=128) == G.ERR_UNSUPPORTED
+    assert dn(K=192) == G.ERR_UNSUPPORTED
     assert dn(ws=None) == G.ERR_WORKSPACE
     need = L.fp8gmm_workspace_bytes(G.OP_TGMM_DENSE, 1024, 256, 128, 3, 0)
     assert need > L.fp8gmm_workspace_bytes(G.OP_TGMM, 1024, 256, 128, 3, 512) + 1024 * (256 + 128)

@@ -291,6 +291,29 @@ def test_tgmm_small_full(grad):
     print(f"tgmm small {grad}: rel fro {tot:.2e} (max per expert {per:.2e})")
 
 
+@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
+def test_tgmm_odd_multiples_of_128(grad):
+    """K and N odd multiples of 128 (the smallest unit the ABI accepts):
+    codes, scales and the f32 gradient against the oracle."""
+    r = np.random.default_rng(384)
+    M, K, N = 1300, 384, 640
+    lhs = W.to_bf16_bits(r.standard_normal((M, K)).astype(np.float32))
+    dout = W.to_bf16_bits(r.standard_normal((M, N)).astype(np.float32) * 1e-3)
+    gs = [513, 0, 200, 511]                       # expert boundaries inside and at tile edges, 76 stale rows
+    W.fill_garbage(lhs, sum(gs))
+    W.fill_garbage(dout, sum(gs))
+    slabs = []
+    (drhs, sL, sD), st = run_tgmm(lhs, dout, gs, grad, ws_out=slabs)
+    assert st == 0
+    n = check_tgmm_codes(lhs, dout, gs, grad, *slabs)
+    ref = O.tgmm_quant(lhs, dout, gs, grad, 512)
+    assert np.array_equal(sL.cpu().numpy()[:n], ref.sL) and np.array_equal(sD.cpu().numpy()[:n], ref.sD)
+    lay = O.layout(gs, M)
+    tot, per = check_f32(drhs.cpu().numpy(), ref.drhs_f64, ref.absum, None, np.minimum(lay.end - lay.start, 512),
+                         f"tgmm {K}x{N} {grad}")
+    print(f"tgmm {K}x{N} {grad}: {n} pairs, rel fro {tot:.2e}")
+
+
 def test_tgmm_stale_tail_and_status():
     lhs, dout = _tgmm_small(6, M=1300)
     gs = [600, 0, 250]

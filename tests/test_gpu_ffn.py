@@ -212,13 +212,24 @@ def check_ffn_stages(d, out, grad, rows=None, cols=None):
     return dict(y=e_y[0], d_preact=e_dz[0], dx=e_dx[0], dwo=e_wo[0], dwi=e_wi[0])
 
 
-@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
-def test_ffn_small_against_oracle(grad):
-    d = W.ffn("small")
+def _ffn_small(grad, key):
+    d = W.ffn(key)
     out = run_ffn(d, grad)
     assert out["status"] == 0
     err = check_ffn_stages(d, out, grad)
-    print(f"ffn small {grad}: " + ", ".join(f"{k} {v:.2e}" for k, v in err.items()))
+    print(f"ffn {key} {grad}: " + ", ".join(f"{k} {v:.2e}" for k, v in err.items()))
+
+
+@pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
+def test_ffn_small_against_oracle(grad):
+    """Ragged experts (one empty) and a garbage tail."""
+    _ffn_small(grad, "small")
+
+
+def test_ffn_sizes_multiple_of_128():
+    """H = 384, I = 128: multiples of 128 but not of 256 (the 128-row tgmm
+    tiles, the cached-block dLHS of a 256-wide contraction)."""
+    _ffn_small("e5m2", "small384")
 
 
 @functools.lru_cache(maxsize=None)

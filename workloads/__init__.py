@@ -226,6 +226,7 @@ def preactivations(config: int, M: int, I2: int, valid: int, std: float = 2.0) -
 FFN_SHAPES = {
     "small": dict(G=4, M=320, valid=None, H=256, I=256),
     "small128": dict(G=4, M=320, valid=None, H=256, I=128),
+    "small384": dict(G=4, M=320, valid=None, H=384, I=128),
     2: dict(G=8, M=8192, valid=8192, H=2048, I=768),
     3: dict(G=32, M=32768, valid=SHAPES[3]["valid"], H=7168, I=2048),
 }
@@ -233,7 +234,7 @@ FFN_SHAPES = {
 
 def _ffn_sizes(key):
     sh = FFN_SHAPES[key]
-    if key in ("small", "small128"):
+    if key in ("small", "small128", "small384"):
         r = rng(90, ROUTING)
         cuts = np.sort(r.integers(0, 257, size=2))
         parts = np.diff(np.concatenate([[0], cuts, [256]]))
@@ -262,7 +263,7 @@ def ffn(key) -> dict:
     G, M, H, I = sh["G"], sh["M"], sh["H"], sh["I"]
     gs = _ffn_sizes(key)
     valid = int(gs.sum())
-    c = 91 if key in ("small", "small128") else key
+    c = 91 if key in ("small", "small128", "small384") else key
     wi_codes, wi_scale = weights(c, FFN_WI, G, H, 2 * I)
     wo_codes, wo_scale = weights(c, FFN_WO, G, I, H)
     return dict(G=G, M=M, H=H, I=I, valid=valid, group_sizes=gs, wi_codes=wi_codes, wi_scale=wi_scale,
