@@ -39,16 +39,16 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 (OCP) MFMA
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes over this bench
-# (profiles/bench_kernels_all_sections.md), scaled by a plain 1 GiB copy: FETCH_SIZE x 2.0,
-# WRITE_SIZE x 1.0.  Each entry holds the hash of the kernel's sources when the counters
-# were taken; once the sources change the figure no longer applies and traffic is null.
+# Bytes per launch through the L2-fabric interface from rocprofv3 FETCH_SIZE / WRITE_SIZE passes over
+# this bench's step (profiles/bench_step_kernels_counters.md), scaled by a plain 1 GiB copy: FETCH_SIZE
+# x 2.0, WRITE_SIZE x 1.0 (MiB read, MiB written).  Each entry holds the hash of the kernel's sources when
+# the counters were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 2757, 77),
+    "wi_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 2742, 77),
     "wo_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 1322, 269),
-    "wi_dlhs": ("dlhs.hip", "f9842814dfd0c577", 2824, 269),
-    "wo_dlhs": ("dlhs.hip", "f9842814dfd0c577", 1427, 77),
-    "tgmm": ("tgmm.hip", "0a83fb49bf493546", 346 + 1139, 181 + 1792),
+    "wi_dlhs": ("dlhs.hip", "92df89c1ec07a5a3", 2823, 269),
+    "wo_dlhs": ("dlhs.hip", "92df89c1ec07a5a3", 1427, 77),
+    "tgmm": ("tgmm.hip", "d3b9100c3d0bb0dd", 346 + 1340, 181 + 1792),
     "dequant": ("dequant.hip", "6ad3c03ff95eea84", 455, 896),
 }
 
