@@ -122,6 +122,15 @@ __device__ __forceinline__ v4i deq8(uint32_t w0, uint32_t w1, float srow) {
                (int)pack_bf16x2(d[0] * row_bcast<8 * H + 6>(srow), d[1] * row_bcast<8 * H + 7>(srow))};
 }
 
+// Output word O (0..7) of a 16-code fragment: the two weights of
+// contraction indices 2O, 2O+1 (deq8<O / 4>'s word O % 4, on its own).
+template <int O>
+__device__ __forceinline__ int deq_word(const v8i& r, float srow) {
+  constexpr int H = O / 4, m = O % 4;
+  const v2f v = dec_e4m3x2<(m & 1) != 0>((uint32_t)r[2 * H + (m >> 1)]);
+  return (int)pack_bf16x2(v[0] * row_bcast<8 * H + 2 * m>(srow), v[1] * row_bcast<8 * H + 2 * m + 1>(srow));
+}
+
 __device__ __forceinline__ float bf16_lo(int v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
 __device__ __forceinline__ float bf16_hi(int v) { return __builtin_bit_cast(float, (uint32_t)v & 0xffff0000u); }
 
@@ -279,9 +288,14 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   // The two waves of a SIMD own the tile's two row halves, so a tile of at
   // most BM/2 valid rows keeps one wave's work per SIMD.
   const bool active = wm * (BM / 2) < rows;
+  // FINE (codes, 256-row tiles): fragment j+1's codes are decoded one output
+  // word per two of fragment j's 16 MFMAs (read two fragments ahead), so the
+  // decode sits between the MFMAs instead of after them.
+  constexpr bool FINE = FROM_CODES && FBK == 8;
   v4i a[FBK][2];
   v4i wcur[2];
-  float scur = 0.f;
+  v8i rawn;           // FINE: the codes of the next fragment, as read
+  float scur = 0.f, sn = 0.f;
   if (active) {
 #pragma unroll
     for (int f = 0; f < FBK; ++f)
@@ -289,6 +303,7 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
       for (int s = 0; s < 2; ++s) a[f][s] = *reinterpret_cast<const v4i*>(slot(0) + a_rd[s] + f * 2048);
     scur = read_s(slot(0));
     convert(scur, read_w(slot(0), 0), wcur);
+    if (FINE) rawn = read_w(slot(0), 1);
   }
 
   static_assert(S == 3, "the copy slot must differ from the two slots read in a stage");
@@ -311,14 +326,55 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
 #pragma unroll
         for (int c = j * C::kLoads / NJ; c < (j + 1) * C::kLoads / NJ; ++c) issue_one(wr, ks + S - 1, c);
       }
-      if (MORE && j == NJ - 1) {
-        // every wave's copy of stage ks+1 has landed (a copy issued at the
-        // top of this stage may still be in flight)
-        if (ISSUE) wait_vmem_lds<C::kLoads>();
+      if (MORE && j == NJ - (FINE ? 2 : 1)) {
+        // every wave's copy of stage ks+1 has landed and every read of this
+        // stage's slot has completed (the copies issued so far in this stage
+        // may still be in flight)
+        if (ISSUE) wait_vmem_lds<((FINE ? NJ - 1 : NJ) * C::kLoads) / NJ>();
         else wait_vmem_lds<0>();
         barrier_only();
       }
-      if constexpr (ACT) {
+      if constexpr (ACT && FINE) {
+        v8i raw2;
+        if (j + 2 < NJ) raw2 = read_w(rd, j + 2);
+        else if (MORE) {
+          raw2 = read_w(rn, j + 2 - NJ);
+          if (j + 2 == NJ) sn = read_s(rn);
+        }
+        const bool conv = j + 1 < NJ || MORE;
+        const float sconv = j + 1 < NJ ? scur : sn;
+        v4i wnext[2];
+        sched_fence();
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+#pragma unroll
+          for (int mm = 2 * o; mm < 2 * o + 2; ++mm) {
+            const int s_ = mm / FBK, f = mm % FBK;
+            acc[f][j] = mfma_bf16_16x16x32(as_bf(wcur[s_]), as_bf(a[f][s_]), acc[f][j]);
+            if (MORE && j == NJ - 1) a[f][s_] = *reinterpret_cast<const v4i*>(rn + a_rd[s_] + f * 2048);
+          }
+          if (conv) {
+            int w;
+            switch (o) {
+              case 0: w = deq_word<0>(rawn, sconv); break;
+              case 1: w = deq_word<1>(rawn, sconv); break;
+              case 2: w = deq_word<2>(rawn, sconv); break;
+              case 3: w = deq_word<3>(rawn, sconv); break;
+              case 4: w = deq_word<4>(rawn, sconv); break;
+              case 5: w = deq_word<5>(rawn, sconv); break;
+              case 6: w = deq_word<6>(rawn, sconv); break;
+              default: w = deq_word<7>(rawn, sconv); break;
+            }
+            wnext[o >> 2][o & 3] = w;
+          }
+          sched_fence();
+        }
+        wcur[0] = wnext[0];
+        wcur[1] = wnext[1];
+        rawn = raw2;
+        if (MORE && j == NJ - 1) scur = sn;
+      }
+      if constexpr (ACT && !FINE) {
         v8i raw;
         float snext = scur;
         if (j + 1 < NJ) raw = read_w(rd, j + 1);
