@@ -46,8 +46,8 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MEASURED_TRAFFIC_MIB = {
     "wi_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 2742, 77),
     "wo_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 1322, 269),
-    "wi_dlhs": ("dlhs.hip", "e2eb5024b10e10af", 2820, 278),
-    "wo_dlhs": ("dlhs.hip", "e2eb5024b10e10af", 1431, 79),
+    "wi_dlhs": ("dlhs.hip", "9f17da007c57a6b0", 2820, 278),
+    "wo_dlhs": ("dlhs.hip", "9f17da007c57a6b0", 1431, 79),
     "tgmm": ("tgmm.hip", "d3b9100c3d0bb0dd", 346 + 1340, 181 + 1792),
     "dequant": ("dequant.hip", "6ad3c03ff95eea84", 455, 896),
 }

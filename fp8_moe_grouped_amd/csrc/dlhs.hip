@@ -26,13 +26,17 @@
 //     contraction), [BN rows][64 codes] or [BN rows][64 bf16], swizzled;
 //   * the 64 scales of the stage (each wave copies eight of them).
 // Every byte reaches LDS through buffer loads with an LDS destination, issued
-// at the top of a stage for two stages ahead; one barrier per stage, just
-// before the next stage is first read.
+// at the top of a stage for two stages ahead; one barrier per stage, before
+// the next stage is first read (on the 256-row code path one fragment before
+// the stage's last, so that the next stage's codes can be read two fragments
+// ahead).
 //
 // Inner loop: a wave keeps its BM/2-row dout operand of the stage in registers
 // and streams its weight fragments (16 output columns each): the next
 // fragment is read from LDS, decoded, scaled and rounded on the VALU between
-// the 16 MFMAs of the current one (the stage's scales are read once, one per
+// the 16 MFMAs of the current one (on the 256-row code path one output word,
+// two weights, after every second MFMA, with scheduling fences between the
+// pieces; the stage's scales are read once, one per
 // lane, and a DPP row broadcast inside each multiply hands every lane the
 // scale of its contraction index); during the
 // last fragment the dout operand of the next stage is reread in place right
