@@ -275,7 +275,7 @@ class TgmmResult:
 
 
 def tgmm_quant(lhs_bits, dout_bits, group_sizes, grad_fmt: str, tile_m: int = 512,
-               k_cols=None, n_cols=None) -> TgmmResult:
+               k_cols=None, n_cols=None, exact: bool = True) -> TgmmResult:
     """Weight-gradient tgmm with in-kernel operand quantization:
     ``drhs[g] = sum_t (sum_{r in T} dec(qL[r,:])^T dec(qD[r,:])) * (sL[t] x sD[t])``
     where for each non-empty (expert, tile) pair T the lhs is quantized to e4m3
@@ -287,6 +287,12 @@ def tgmm_quant(lhs_bits, dout_bits, group_sizes, grad_fmt: str, tile_m: int = 51
 
     ``k_cols``/``n_cols`` restrict the output to some columns; every channel's
     scale depends only on its own column, so the restriction is exact.
+
+    ``exact=False`` forms the tile sums with a float64 matrix product of the
+    same integer-valued operands instead of int64 arithmetic (for the largest
+    shapes): every product is exact in float64, and a sum of at most
+    ``tile_m`` of them is within ``tile_m * 2**-53`` of the sum of their
+    magnitudes, far below the f32 rounding of the result.
     """
     lhs_bits = np.asarray(lhs_bits); dout_bits = np.asarray(dout_bits)
     M, K = lhs_bits.shape
@@ -310,6 +316,8 @@ def tgmm_quant(lhs_bits, dout_bits, group_sizes, grad_fmt: str, tile_m: int = 51
         qD = quantize_cols(xd, sD, grad_fmt)
         iL = (F.decode(qL, F.E4M3) * 2.0 ** _INT_SHIFT[F.E4M3]).astype(np.int64)
         iD = (F.decode(qD, grad_fmt) * 2.0 ** _INT_SHIFT[grad_fmt]).astype(np.int64)
+        if not exact:
+            iL, iD = iL.astype(np.float64), iD.astype(np.float64)
         tile_sum = (iL.T @ iD).astype(np.float64) * 2.0 ** -(_INT_SHIFT[F.E4M3] + _INT_SHIFT[grad_fmt])
         tile_abs = (np.abs(iL).T @ np.abs(iD)).astype(np.float64) * 2.0 ** -(_INT_SHIFT[F.E4M3] + _INT_SHIFT[grad_fmt])
         outer = sL.astype(np.float64)[:, None] * sD.astype(np.float64)[None, :]

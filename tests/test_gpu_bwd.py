@@ -367,6 +367,26 @@ def test_tgmm_config4_sampled(grad):
     print(f"tgmm config4 {grad}: {len(tiles)} pairs, rel fro {tot:.2e} (max per expert {per:.2e})")
 
 
+CFG4_K_CHUNKS = 4
+
+
+@pytest.mark.parametrize("grad,chunk", [(g_, c) for g_ in ("e5m2", "e4m3") for c in range(CFG4_K_CHUNKS)])
+def test_tgmm_config4_all_columns(grad, chunk):
+    """The dropless buffer: every element of the f32 gradient (a quarter of
+    the k columns per case, all n columns, every expert) against the oracle,
+    whose tile sums come from float64 products of the integer-valued codes
+    here (within 512 * 2^-53 of the exact sums, pinned on the CPU)."""
+    d, drhs, _, _, _, _, st = _cfg4_tgmm(grad)
+    assert st == 0
+    kc = np.array_split(np.arange(d["K"]), CFG4_K_CHUNKS)[chunk]
+    ref = O.tgmm_quant(d["lhs"], d["dout"], d["group_sizes"], grad, 512, k_cols=kc, exact=False)
+    got = drhs[:, int(kc[0]):int(kc[-1]) + 1].cpu().numpy()
+    lay = O.layout(d["group_sizes"], d["M"])
+    tot, per = check_f32(got, ref.drhs_f64, ref.absum, None, np.minimum(lay.end - lay.start, 512),
+                         f"tgmm cfg4 k {kc[0]}..{kc[-1]}")
+    print(f"tgmm config4 {grad} k {kc[0]}..{kc[-1]}: rel fro {tot:.2e} (max per expert {per:.2e})")
+
+
 @pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
 def test_tgmm_config4_codes(grad):
     """The dropless buffer: the lhs and gradient codes of every (expert, tile)

@@ -435,6 +435,28 @@ def test_tgmm_lossless_construction(grad_fmt):
         assert np.array_equal(res.drhs[g], ref), g
 
 
+@pytest.mark.parametrize("grad_fmt", [F.E5M2, F.E4M3])
+def test_tgmm_float64_products_match_exact_sums(grad_fmt):
+    """The float64-product path (for the largest shapes) against the exact
+    integer sums: full 512-row tiles of seeded data with outliers, so the
+    products span many binades; the difference stays within 512 * 2^-53 of
+    the magnitude sum, and the f32 results agree."""
+    r = np.random.default_rng(19)
+    M, K, N = 1300, 48, 40
+    sizes = [600, 0, 700]
+    x = r.standard_normal((M, K)).astype(np.float32)
+    x[r.integers(0, M, 60), r.integers(0, K, 60)] *= 50
+    lhs = bf16_bits(x)
+    dout = bf16_bits((r.standard_normal((M, N)) * 1e-3).astype(np.float32))
+    ex = O.tgmm_quant(lhs, dout, sizes, grad_fmt, 512)
+    fp = O.tgmm_quant(lhs, dout, sizes, grad_fmt, 512, exact=False)
+    assert np.array_equal(ex.sL, fp.sL) and np.array_equal(ex.sD, fp.sD)
+    assert np.all(np.abs(fp.drhs_f64 - ex.drhs_f64) <= 512 * 2.0 ** -53 * ex.absum + 1e-300)
+    assert np.array_equal(fp.absum, ex.absum)
+    mism = np.count_nonzero(fp.drhs != ex.drhs)
+    assert mism <= 2, mism     # at most a rare tie of the final f32 rounding
+
+
 def test_tgmm_stale_tail_and_tiles():
     from workloads import fill_garbage
     r = np.random.default_rng(18)
