@@ -397,6 +397,62 @@ def skinny_groups(G, stream, codes_wi, scale_wi, codes_wo, scale_wo, rows_per_ex
     return out
 
 
+def small_configs(G, stream):
+    """The small configurations (µs-scale calls, where launches and the amax
+    pass weigh): config 0 forward (G=4, M=256, K=128, N=256), config 1 wi
+    forward with SwiGLU (G=8, M=8192, K=2048, N=2x768), config 2 wo forward
+    and its dLHS (G=8, M=8192, K=768, N=2048), all rows valid.  Each call is
+    timed with HIP events over 50 calls after 5 warmups (quantizer included in
+    the forwards); the roofline time is the larger of flops at the MFMA peak
+    (FP8 forward, bf16 dLHS) and the algorithmic bytes at the HBM peak."""
+    import torch
+    import workloads as W
+
+    def timed(fn, n=50):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {"workload": "configs 0-2 (all rows valid), 50 calls each after 5 warmups"}
+    for name, cfg, op in (("cfg0_fwd", 0, "fwd"), ("cfg1_wi_fwd", 1, "wi"), ("cfg2_wo_fwd", 2, "wo"),
+                          ("cfg2_wo_dlhs", 2, "dlhs_wo")):
+        d = W.make(cfg, op)
+        Gn, M, K, N = d["G"], len(d["lhs"]) if "lhs" in d else len(d["dout"]), d["K"], d["N"]
+        gs = to_dev(np.asarray(d["group_sizes"], np.int32))
+        codes, scale = to_dev(d["codes"]), to_dev(d["scale"])
+        flops = 2.0 * M * K * N
+        if op == "dlhs_wo":
+            dout = to_dev(d["dout"])
+            res = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+            fn = lambda: G.gmm_dlhs_fp8(dout, codes, scale, gs, out=res)
+            nbytes = M * N * 2 + Gn * K * N + Gn * N * 4 + M * K * 2
+            peak = BF16_PEAK_TFLOPS
+        else:
+            x = to_dev(d["lhs"])
+            swiglu = op == "wi"
+            res = torch.empty((M, N // 2 if swiglu else N), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(G.workspace_bytes(G.OP_SILU if swiglu else G.OP_FWD, M, K, N, Gn), dtype=torch.uint8,
+                             device="cuda")
+            if swiglu:
+                fn = lambda: G.gmm_silu_fp8(x, codes, scale, gs, out=res, workspace=ws)
+            else:
+                fn = lambda: G.gmm_fp8_fwd(x, codes, scale, gs, out=res, workspace=ws)
+            nbytes = M * K * 2 + Gn * K * N + Gn * N * 4 + res.numel() * 2
+            peak = FP8_PEAK_TFLOPS
+        ms = timed(fn)
+        roof_us = max(flops / (peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)) * 1e6
+        out[name] = {"us": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "roofline_us": round(roof_us, 2), "frac_roofline": round(roof_us / (ms * 1e3), 3)}
+    return out
+
+
 def lhs_quant_variants(G, stream, x, codes, scale, gs, mv):
     """The forward's ops-level LHS-quantization variants on the dropless wi
     input (K = 7168, N = 4096 without SwiGLU): quantizer + GEMM per call."""
@@ -574,6 +630,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the buffer-wide tgmm baseline")
     ap.add_argument("--no-vendor", action="store_true", help="skip the vendor dense-GEMM reference")
     ap.add_argument("--no-skinny", action="store_true", help="skip the skinny-groups (decode-like) measurement")
+    ap.add_argument("--no-small", action="store_true", help="skip the small configurations (configs 0-2)")
     ap.add_argument("--no-sclk", action="store_true", help="skip the shader-clock sampling")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy (read MIB, write MIB) three times; used to scale "
@@ -754,6 +811,7 @@ def main():
     micro = None if args.no_micro else pages_microbench(G, stream)
     vendor = None if args.no_vendor else vendor_dense(stream, mv, kern["wi_gemm"]["ms"], ops["wi_dlhs"]["ms"])
     skinny = None if args.no_skinny else skinny_groups(G, stream, codes_wi, scale_wi, codes_wo, scale_wo)
+    small = None if args.no_small else small_configs(G, stream)
     ffn = None if args.no_ffn else ffn_step(G, args, gs, lhs_wi, codes_wi, scale_wi, codes_wo, scale_wo, dout_wo,
                                             int(np.sum(d["gs"])), stream)
 
@@ -795,6 +853,7 @@ def main():
         "sclk_during_steps": sclk,
         "vendor_dense": vendor,
         "skinny_groups": skinny,
+        "small_configs": small,
     }
     print(json.dumps(line), flush=True)
 
