@@ -180,6 +180,35 @@ __device__ __forceinline__ void barrier_only() {
 // prefetch stays ahead of the MFMAs it is meant to overlap.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Issue priority by progress.  The two waves of a SIMD leave each stage
+// barrier together, and among waves of equal priority the sequencer issues
+// the older one first, so the younger wave ends every stage alone and the
+// older one waits for it at the next barrier (measured on the tgmm: the
+// younger waves' stage bodies took 1.5x as long).  A loop body in P pieces
+// between two barriers calls this at the start of piece P (0 = just past the
+// barrier): the wave that is behind gets the higher priority, which keeps the
+// two waves within about one piece of each other.  Priority 0 is restored
+// after the loop.
+template <int P>
+__device__ __forceinline__ void prio_by_progress() {
+  static_assert(P >= 0, "piece index");
+  if constexpr (P == 0) __builtin_amdgcn_s_setprio(3);
+  else if constexpr (P == 1) __builtin_amdgcn_s_setprio(2);
+  else if constexpr (P == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// The same for a piece index known only after unrolling (p < 4 selects the
+// level, larger values take priority 0).
+__device__ __forceinline__ void prio_by_progress(int p) {
+  switch (p) {
+    case 0: prio_by_progress<0>(); break;
+    case 1: prio_by_progress<1>(); break;
+    case 2: prio_by_progress<2>(); break;
+    default: prio_by_progress<3>(); break;
+  }
+}
+
 // Ask the scheduler for a group of `n` instructions of the classes in `mask`
 // (0x2 VALU, 0x8 MFMA, 0x100 LDS read, 0x20 VMEM read) at this point of the
 // sequence; consecutive calls with the same id interleave the classes.

@@ -326,6 +326,8 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     constexpr bool ACT = decltype(act_c)::value;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      // pieces counted from the fragment the stage barrier precedes
+      prio_by_progress((j - (FINE ? NJ - 2 : NJ - 1) + NJ) % NJ);
       if (ISSUE) {
 #pragma unroll
         for (int c = j * C::kLoads / NJ; c < (j + 1) * C::kLoads / NJ; ++c) issue_one(wr, ks + S - 1, c);
@@ -411,6 +413,7 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
   };
   if (active) run(T_{});
   else run(F_{});
+  prio_by_progress<3>();
 
   // ---- epilogue: lane owns row wm*128 + f*16 + lane%16, columns wn*BN/4 + j*16 + 4*(lane/16) + 0..3
   // Lanes l and l^16 hold the same row, columns 4q..4q+3 and 4q+4..4q+7 (q even)

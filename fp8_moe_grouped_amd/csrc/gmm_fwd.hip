@@ -339,6 +339,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      prio_by_progress(j);
       if (ISSUE) {
 #pragma unroll
         for (int q = j * kLoads / NJ; q < (j + 1) * kLoads / NJ; ++q) issue_one(wr, ks + kStages, q);
@@ -379,6 +380,7 @@ void gmm_fp8_fwd_kernel(const uint8_t* __restrict__ aq, const float* __restrict_
   };
   if (active) run(T_{});
   else run(F_{});
+  prio_by_progress<3>();
 
   // ---- epilogue: lane owns row wm*64 + i*32 + lane%32 and, per fragment j,
   // columns tc(j) + 8*q + 4*(lane/32) + 0..3 for q = 0..3

@@ -469,6 +469,7 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (s >= nsub) break;     // a pair's last stage: rows past its 32-row padding are not computed
+    prio_by_progress(s);
     v2i cb[4], ca[4];
     if (s + 1 < NS) {
 #pragma unroll
@@ -488,6 +489,7 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
       for (int f = 0; f < 4; ++f) ao[f] = widen8<false>(ca[f]);
     }
   }
+  prio_by_progress<3>();
   if (last) {
     // pair complete: total += partial * sL[k] * sD[n]
     float slv[4];
