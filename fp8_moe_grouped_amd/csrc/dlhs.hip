@@ -348,7 +348,12 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
           if (j + 2 == NJ) sn = read_s(rn);
         }
         const bool conv = j + 1 < NJ || MORE;
-        const float sconv = j + 1 < NJ ? scur : sn;
+        // a fresh copy of the scale per fragment: without it the compiler
+        // shares each lane broadcast between the fragments of a stage, and a
+        // broadcast with several uses is not folded into its multiply (a
+        // v_mov_dpp and a zeroing move per weight instead of none)
+        float sconv = j + 1 < NJ ? scur : sn;
+        asm volatile("" : "+v"(sconv));
         v4i wnext[2];
         sched_fence();
 #pragma unroll
