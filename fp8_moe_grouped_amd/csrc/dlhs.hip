@@ -24,7 +24,8 @@
 //   * the dout tile, [BM rows][64 bf16], 16-byte chunks XOR-swizzled;
 //   * the weight tile in its natural [k][n] layout (n contiguous, which is the
 //     contraction), [BN rows][64 codes] or [BN rows][64 bf16], swizzled;
-//   * the 64 scales of the stage (each wave copies eight of them).
+//   * the 64 scales of the stage (every wave copies all of them, the same
+//     bytes to the same place, so the copy needs no per-lane branch).
 // Every byte reaches LDS through buffer loads with an LDS destination, issued
 // at the top of a stage for two stages ahead; one barrier per stage, before
 // the next stage is first read (on the 256-row code path one fragment before
@@ -232,8 +233,12 @@ void gmm_dlhs_kernel(const uint16_t* __restrict__ dout, const uint8_t* __restric
     } else if (c < C::kALoads + C::kWLoads) {
       const int j = c - C::kALoads;
       dma16(rw, St + C::kABytes + (C::kWLoads * wave + j) * 1024, vw[j], (uint32_t)ks * C::kWRow);
-    } else if (lane < 8) {     // this wave's eight of the stage's 64 scales
-      dma4(rs, St + C::kABytes + C::kWBytes + wave * 32, (uint32_t)(wave * 8 + lane) * 4u, (uint32_t)ks * 256u);
+    } else {
+      // the stage's 64 scales, copied whole by every wave (the same bytes to the
+      // same place): a per-lane condition here would split the stage's code at a
+      // divergent branch, and the scale broadcasts of the decode are then no
+      // longer folded into their multiplies
+      dma4(rs, St + C::kABytes + C::kWBytes, (uint32_t)lane * 4u, (uint32_t)ks * 256u);
     }
   };
   // weight fragment j as read from LDS (codes: 16 bytes; bf16: 2 x 16 bytes)
