@@ -44,12 +44,14 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # x 2.0, WRITE_SIZE x 1.0 (MiB read, MiB written).  Each entry holds the hash of the kernel's sources when
 # the counters were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 2742, 77),
-    "wo_gemm": ("gmm_fwd.hip", "c1f6a72223475225", 1322, 269),
-    "wi_dlhs": ("dlhs.hip", "9f17da007c57a6b0", 2820, 278),
-    "wo_dlhs": ("dlhs.hip", "9f17da007c57a6b0", 1431, 79),
-    "tgmm": ("tgmm.hip", "d3b9100c3d0bb0dd", 346 + 1340, 181 + 1792),
-    "dequant": ("dequant.hip", "6ad3c03ff95eea84", 455, 896),
+    "wi_gemm": ("gmm_fwd.hip", "638821bf2a683269", 2631, 77),
+    "wo_gemm": ("gmm_fwd.hip", "638821bf2a683269", 1311, 269),
+    "wi_dlhs": ("dlhs.hip", "b375ab74f394f0f9", 2815, 269),
+    "wo_dlhs": ("dlhs.hip", "b375ab74f394f0f9", 1427, 77),
+    "tgmm": ("tgmm.hip", "35fcc4f20ffd3a15", 346 + 1324, 181 + 1792),
+    "dequant": ("dequant.hip", "ee5353dbbb419772", 455, 896),
+    "wi_quant": ("quant.hip", "77d3c3d659416414", 269, 135),
+    "wo_quant": ("quant.hip", "77d3c3d659416414", 77, 39),
 }
 
 
@@ -744,22 +746,32 @@ def main():
     for k in ("wi_quant", "wo_quant", "dequant"):
         kern[k]["gbs"] = by[k] / (op_ms[k] * 1e-3) / 1e9
 
-    # dominant kernel by time and its roofline
+    # every timed item of the step against its own roofline; the dominant one (by time) is `roofline`.
+    # The tgmm item is one call of two launches (the operand prep, then the GEMM), timed together.
+    launched = {"wi_quant": "quant_rows_e4m3_kernel<16>", "wi_gemm": "gmm_fp8_fwd_kernel<false, true, 256>",
+                "wo_quant": "quant_rows_e4m3_kernel<4>", "wo_gemm": "gmm_fp8_fwd_kernel<false, false, 256>",
+                "wo_dlhs": "gmm_dlhs_kernel (wo, 256 x 256 tiles)", "wi_dlhs": "gmm_dlhs_kernel (wi, 256 x 256 tiles)",
+                "tgmm": "tgmm_prep_kernel<true> + tgmm_gemm_kernel<true, 256>", "dequant": "dequant_kernel<true>"}
+
+    def roofline_of(k):
+        if k in ("wi_gemm", "wo_gemm"):
+            f = fl["wi_fwd"] if k == "wi_gemm" else fl["wo_fwd"]
+            r = {"bound": "mfma", "achieved": tfs(f, op_ms[k]), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        elif k in ("wi_dlhs", "wo_dlhs"):
+            r = {"bound": "mfma", "achieved": tfs(fl[k], op_ms[k]), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            r = {"bound": "hbm", "achieved": by[k] / (op_ms[k] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        r["frac"] = r["achieved"] / r["peak"]
+        r["ms"] = op_ms[k]
+        r["kernels"] = launched.get(k, k)
+        return r
+
     dom = max(names, key=lambda k: op_ms[k])
-    if dom in ("wi_gemm", "wo_gemm"):
-        f = fl["wi_fwd"] if dom == "wi_gemm" else fl["wo_fwd"]
-        roof = {"kernel": dom, "bound": "mfma", "achieved": tfs(f, op_ms[dom]), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    elif dom in ("wi_dlhs", "wo_dlhs"):
-        roof = {"kernel": dom, "bound": "mfma", "achieved": tfs(fl[dom], op_ms[dom]), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": by[dom] / (op_ms[dom] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof = {"kernel": dom, **roofline_of(dom)}
     roof["traffic"] = measured_traffic(dom)
     roof["traffic_unit"] = ("bytes per launch through the L2-fabric interface (rocprofv3 FETCH_SIZE x 2.0 + "
                             "WRITE_SIZE, calibrated on a 1 GiB copy); Infinity Cache hits included")
+    roof_all = {k: {**roofline_of(k), "traffic": measured_traffic(k)} for k in names}
 
     # bf16 arm: same scheduler, weights dequantized beforehand (not timed)
     ratio = None
@@ -840,6 +852,8 @@ def main():
             "gemm_tflop_per_step": round(total_flops / 1e12, 4),
         },
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
+        "roofline_all": {n: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                         for n, r in roof_all.items()},
         "cpu_baseline": cpu,
         "ops": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()} for k, v in ops.items()},
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kern.items()},
