@@ -452,13 +452,20 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
                                            const StageCopy<C>& cp, int wave, const int* a_rd, const int* b_rd,
                                            int nsub, bool last, int sl_rd, int sd_rd, v4f (&part)[4][4],
                                            v4f (&tot)[4][4]) {
-  if (copy) {
-#pragma unroll
-    for (int j = 0; j < C::kALoads; ++j) dma16(cp.ra, wr + (C::kALoads * wave + j) * 1024, cp.va[j], cp.soa);
-#pragma unroll
-    for (int j = 0; j < C::kBLoads; ++j) dma16(cp.rb, wr + C::kAStage + (C::kBLoads * wave + j) * 1024, cp.vb[j], cp.sob);
-    dma4(cp.rs, wr + C::kAStage + C::kBStage + cp.s_lds, cp.vs, 0);
-  }
+  // The copy of a later stage is spread over the sub-steps (copy q goes out
+  // at the top of sub-step q * NS / kLoads): issued all at once, the eight
+  // waves' 56 copies queue behind each other in the CU's address unit and the
+  // last waves wait there for most of a sub-step before their first MFMA.
+  auto issue_copy = [&](int q) __attribute__((always_inline)) {
+    if (q < C::kALoads) {
+      dma16(cp.ra, wr + (C::kALoads * wave + q) * 1024, cp.va[q], cp.soa);
+    } else if (q < C::kALoads + C::kBLoads) {
+      const int j = q - C::kALoads;
+      dma16(cp.rb, wr + C::kAStage + (C::kBLoads * wave + j) * 1024, cp.vb[j], cp.sob);
+    } else {
+      dma4(cp.rs, wr + C::kAStage + C::kBStage + cp.s_lds, cp.vs, 0);
+    }
+  };
   // Sub-steps are software-pipelined: the codes of sub-step s+1 are read
   // before sub-step s's MFMAs and widened after them.
   v4i bo[4], ao[4];
@@ -470,6 +477,11 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
   for (int s = 0; s < NS; ++s) {
     if (s >= nsub) break;     // a pair's last stage: rows past its 32-row padding are not computed
     prio_by_progress(s);
+    if (copy) {
+#pragma unroll
+      for (int q = 0; q < C::kLoads; ++q)
+        if (q * NS / C::kLoads == s) issue_copy(q);
+    }
     v2i cb[4], ca[4];
     if (s + 1 < NS) {
 #pragma unroll
@@ -490,6 +502,11 @@ __device__ __forceinline__ void tgmm_stage(uint8_t* __restrict__ wr, const uint8
     }
   }
   prio_by_progress<3>();
+  if (copy && nsub < NS) {   // the copies of the sub-steps a short stage does not run
+#pragma unroll
+    for (int q = 0; q < C::kLoads; ++q)
+      if (q * NS / C::kLoads >= nsub) issue_copy(q);
+  }
   if (last) {
     // pair complete: total += partial * sL[k] * sD[n]
     float slv[4];
