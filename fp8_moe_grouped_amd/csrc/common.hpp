@@ -153,17 +153,20 @@ __device__ __forceinline__ void wait_vmem_lds() {
 }
 
 // x / s for the quantizers, from r = 1/s (correctly rounded, one division per
-// scale): q0 = x*r, the residual x - q0*s (exact through the fma), one
-// correction, and x's sign (so that -0 stays -0).  Over the quantizers' inputs
-// -- x a bf16 value with |x| <= amax, s = f32(max(amax, 1e-12) / FMAX), FMAX
-// 448 or 57344, amax finite -- the result equals the IEEE quotient wherever the
+// scale): q0 = x*r, the negated residual q0*s - x (exact through the fma) and
+// one correction.  Negating the residual keeps the sign of a zero x through
+// the last fma (-0 stays -0) without a copysign; the result has the same bits
+// as copysign(fma(x - q0*s, r, q0), x).  Over the quantizers' inputs -- x a
+// bf16 value with |x| <= amax, s = f32(max(amax, 1e-12) / FMAX), FMAX 448 or
+// 57344, amax finite -- the result equals the IEEE quotient wherever the
 // quotient is at least half the smallest subnormal code of the format (below
-// that both encode to zero): tests/test_div_by_scale.py checks every such pair.
-// s must be finite; callers divide directly otherwise.
+// that both encode to zero): tests/test_div_by_scale.py checks every such pair
+// (and the equality with the copysign form).  s must be finite; callers divide
+// directly otherwise.
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   const float q0 = x * r;
-  const float e = __builtin_fmaf(-q0, s, x);
-  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+  const float en = __builtin_fmaf(q0, s, -x);
+  return __builtin_fmaf(-en, r, q0);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): it does not
