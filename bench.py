@@ -44,14 +44,14 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # x 2.0, WRITE_SIZE x 1.0 (MiB read, MiB written).  Each entry holds the hash of the kernel's sources when
 # the counters were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "638821bf2a683269", 2631, 77),
-    "wo_gemm": ("gmm_fwd.hip", "638821bf2a683269", 1311, 269),
-    "wi_dlhs": ("dlhs.hip", "b375ab74f394f0f9", 2815, 269),
-    "wo_dlhs": ("dlhs.hip", "b375ab74f394f0f9", 1427, 77),
-    "tgmm": ("tgmm.hip", "35fcc4f20ffd3a15", 346 + 1324, 181 + 1792),
-    "dequant": ("dequant.hip", "ee5353dbbb419772", 455, 896),
-    "wi_quant": ("quant.hip", "77d3c3d659416414", 269, 135),
-    "wo_quant": ("quant.hip", "77d3c3d659416414", 77, 39),
+    "wi_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 2633, 77),
+    "wo_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 1308, 269),
+    "wi_dlhs": ("dlhs.hip", "8935edf5202e04f8", 2815, 269),
+    "wo_dlhs": ("dlhs.hip", "8935edf5202e04f8", 1427, 77),
+    "tgmm": ("tgmm.hip", "9ff352278f376898", 346 + 1354, 181 + 1792),
+    "dequant": ("dequant.hip", "f9f30637c789a9b5", 455, 896),
+    "wi_quant": ("quant.hip", "684bab8ddb83acb4", 269, 135),
+    "wo_quant": ("quant.hip", "684bab8ddb83acb4", 77, 39),
 }
 
 
