@@ -462,6 +462,17 @@ def tgmm_workspace_codes(workspace, M, K, N, G, tile_m=512):
     return ql, qd
 
 
+def tgmm_workspace_deal(workspace, M, K, N, G, tile_m=512):
+    """View of the GEMM's work-item deal a tgmm_quant call left in its
+    workspace (the layout the header documents): int32 [G] block offsets."""
+    tmax = -(-M // tile_m) + G - 1
+    al = lambda x: (x + 255) // 256 * 256
+    off = al(tmax * tile_m * K) + al(tmax * tile_m * N) + al(tmax * K * 4) + al(tmax * N * 4)
+    if workspace.numel() < off + 4 * G or tmax <= 0:
+        raise ValueError("workspace too small for these sizes")
+    return workspace[off: off + 4 * G].view(torch.int32)
+
+
 def tgmm_dense_quant(lhs, dout, group_sizes, grad_dtype="e5m2", *, out=None, debug=False, dev_status=None,
                      workspace=None):
     """The buffer-wide backward quantization baseline (every row of the

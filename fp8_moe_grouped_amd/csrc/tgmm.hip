@@ -15,11 +15,12 @@
 //     the pair's valid rows once, reduces the column amax (wave shuffles +
 //     LDS), writes the scales and stores the 8-bit codes row-major into the
 //     pair's slab of the workspace ([512 rows][columns], rows past the pair's
-//     end up to the next multiple of 32 hold zero codes).
+//     end up to the next multiple of 32 hold zero codes).  One block of it
+//     also computes the GEMM's item deal (build_item_schedule) meanwhile.
 //  2. gemm: persistent, walking each block's share of the work items
 //     (expert, k tile of 256 rows -- 128 when K is not a multiple of 256 --,
-//     128-column n tile); an item covers the expert's pairs 128 (64) rows at
-//     a time.  The code chunks of both operands are copied HBM -> LDS by
+//     128-column n tile), dealt so that the blocks' modelled loads stay even;
+//     an item covers the expert's pairs 128 (64) rows at a time.  The code chunks of both operands are copied HBM -> LDS by
 //     buffer loads with an LDS destination through a three- (four-) stage
 //     ring that runs across pairs and items, so copy latency is
 //     paid once per block rather than once per tile; a pair's last stage
@@ -109,6 +110,93 @@ __device__ __forceinline__ int pair_group(const PairTable& t, int G, int p) {
   return lo;
 }
 
+// Item deal of the GEMM (tgmm_gemm_kernel): expert g's work item j goes to
+// block (o_g + j) mod nb.  Every block gets per_g / nb items of each expert,
+// and the per_g mod nb that remain go to nb-consecutive (cyclic) blocks from
+// o_g.  Plain round-robin over the item index (o_g = g * per_g mod nb) lets
+// the blocks that draw the heavy experts' remainders run ~6 % longer than
+// the mean on a Zipf routing; here the experts are taken by decreasing cost
+// and each one's remainder starts at the least-loaded window so far, which
+// brings a simulated max/mean to within 1 %.  The cost of an item is a model
+// of the GEMM's time per item from per-wave timers (ticks per 32-row sub-step,
+// per ring stage, per pair-end rescale and per tile store).
+constexpr int kMaxSchedGroups = 256;   // larger G keeps the round-robin deal
+constexpr int kMaxSchedBlocks = 512;   // the GEMM's grid: one or two blocks per CU
+constexpr int kCostSub = 730, kCostStage = 1300, kCostPair = 1100, kCostItem = 5930;
+
+// Run by every thread of one block (blockDim.x >= 64, a multiple of 64) after
+// the pair table is in LDS; writes sched[g] = o_g for every expert.
+__device__ void build_item_schedule(const PairTable& pt, int G, int chunk, int per_g, int nb,
+                                    int* __restrict__ sched) {
+  __shared__ int s_cost[kMaxSchedGroups], s_order[kMaxSchedGroups];
+  __shared__ int s_pre[kMaxSchedBlocks + 1];   // s_pre[t]: load of blocks [0, t) from the remainders dealt so far
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int g = tid; g < G; g += nt) {
+    int c = kCostItem;
+    for (int p = pt.p_base[g]; p < pt.p_base[g + 1]; ++p) {
+      int r0, r1;
+      pair_rows(pt, g, p, r0, r1);
+      const int sub = (r1 - r0 + kSub - 1) / kSub;
+      c += kCostSub * sub + kCostStage * ((sub * kSub + chunk - 1) / chunk) + kCostPair;
+    }
+    s_cost[g] = (c + 255) >> 8;   // units of 256 ticks: the prefix sums stay within 32 bits
+  }
+  for (int t = tid; t <= nb; t += nt) s_pre[t] = 0;
+  __syncthreads();
+  for (int g = tid; g < G; g += nt) {   // rank by decreasing cost, ties by expert index
+    const int c = s_cost[g];
+    int r = 0;
+    for (int h = 0; h < G; ++h) {
+      const int ch = s_cost[h];
+      r += (ch > c) || (ch == c && h < g);
+    }
+    s_order[r] = g;
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid, extra = per_g % nb, per_lane = (nb + 63) / 64, t0 = lane * per_lane;
+  for (int i = 0; i < G; ++i) {
+    const int g = s_order[i];
+    int bo = 0;
+    if (extra != 0) {
+      // the window [o, o + extra) (cyclic) with the smallest load; the smallest o on ties
+      int best = 0x7fffffff;
+      const int tot = s_pre[nb];
+      for (int k = 0; k < per_lane; ++k) {
+        const int o = t0 + k;
+        if (o < nb) {
+          const int e = o + extra;
+          const int w = e <= nb ? s_pre[e] - s_pre[o] : tot - s_pre[o] + s_pre[e - nb];
+          if (w < best) {
+            best = w;
+            bo = o;
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const int wb = __shfl_xor(best, off, 64), ob = __shfl_xor(bo, off, 64);
+        if (wb < best || (wb == best && ob < bo)) {
+          best = wb;
+          bo = ob;
+        }
+      }
+      // add the expert's cost to the window's blocks: s_pre[t] += c * |window intersect [0, t)|
+      // (lane L owns entries [L * per_lane, (L + 1) * per_lane) up to nb; lane 63 also owns nb when
+      // the lanes' ranges end exactly there)
+      const int c = s_cost[g], end = bo + extra;
+      auto add = [&](int t) {
+        const int n = end <= nb ? min(max(t - bo, 0), extra) : min(max(t - bo, 0), nb - bo) + min(t, end - nb);
+        s_pre[t] += c * n;
+      };
+      for (int k = 0; k < per_lane; ++k)
+        if (t0 + k <= nb) add(t0 + k);
+      if (lane == 63 && 64 * per_lane == nb) add(nb);
+    }
+    if (lane == 0) sched[g] = bo;
+  }
+}
+
 // ------------------------------------------------------------------ prep
 
 template <bool GRAD_E5M2>
@@ -117,7 +205,8 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
                                                              const int* __restrict__ group_sizes, int G, int M,
                                                              int K, int N, uint8_t* __restrict__ ql,
                                                              uint8_t* __restrict__ qd, float* __restrict__ sl,
-                                                             float* __restrict__ sd, int* status) {
+                                                             float* __restrict__ sd, int* status, int* sched,
+                                                             int s_chunk, int s_per_g, int s_nb) {
   __shared__ int g_start[kMaxGroups + 1], p_base[kMaxGroups + 1];
   __shared__ float red[4][kPrepCols];
   PairTable pt{g_start, p_base};
@@ -125,6 +214,8 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
   // read neighbouring strips of the same rows), blockIdx.y = pair
   build_pair_table(group_sizes, G, M, pt, blockIdx.x == 0 ? status : nullptr);
   __syncthreads();
+  // the GEMM's item deal, by one block while the others quantize
+  if (sched != nullptr && blockIdx.x == 0 && blockIdx.y == 0) build_item_schedule(pt, G, s_chunk, s_per_g, s_nb, sched);
   const int p = blockIdx.y;
   if (p >= p_base[G]) return;
   const int g = pair_group(pt, G, p);
@@ -329,11 +420,13 @@ __global__ __launch_bounds__(kThreads) void dense_gather_kernel(const uint8_t* _
                                                                 const int* __restrict__ group_sizes, int G, int M,
                                                                 int K, int N, uint8_t* __restrict__ ql,
                                                                 uint8_t* __restrict__ qd, float* __restrict__ sl,
-                                                                float* __restrict__ sd, int* status) {
+                                                                float* __restrict__ sd, int* status, int* sched,
+                                                                int s_chunk, int s_per_g, int s_nb) {
   __shared__ int g_start[kMaxGroups + 1], p_base[kMaxGroups + 1];
   PairTable pt{g_start, p_base};
   build_pair_table(group_sizes, G, M, pt, blockIdx.y == 0 ? status : nullptr);
   __syncthreads();
+  if (sched != nullptr && blockIdx.x == 0 && blockIdx.y == 0) build_item_schedule(pt, G, s_chunk, s_per_g, s_nb, sched);
   const int p = blockIdx.x;
   if (p >= p_base[G]) return;
   const int g = pair_group(pt, G, p);
@@ -397,8 +490,9 @@ struct TgCfg {
   static constexpr int kARows = 1024 / BMK;                   // qL rows per 1 KB load
   static constexpr int kAChunks = BMK / 16;                   // 16-byte chunks per qL row
   static constexpr int kSlicesL = BMK / 64;                   // 256-byte sL slices per stage
-  static_assert(kBlocksPerCU * (kLds + sizeof(int) * 2 * (kMaxGroups + 1)) <= 160 * 1024,
-                "the rings and expert tables of a CU's blocks fit the LDS");
+  static_assert(kBlocksPerCU * (kLds + sizeof(int) * 2 * (kMaxGroups + 1) + sizeof(uint16_t) * kMaxGroups) <=
+                    160 * 1024,
+                "the rings, expert tables and item offsets of a CU's blocks fit the LDS");
   static_assert(kLoads * (kStages - 1) < 64, "outstanding copies fit vmcnt");
   // 16-byte chunk swizzles: the 16 lanes of a transposing read touch 8
   // consecutive rows at one chunk, and two such groups are served together.
@@ -531,8 +625,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(TgCfg<BMK_>::kThreads, TgC
                           amdgpu_waves_per_eu(2, 2)))
 void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict__ qd,
                       const float* __restrict__ sl, const float* __restrict__ sd,
-                      const int* __restrict__ group_sizes, int G, int M, int K, int N,
-                      float* __restrict__ drhs) {
+                      const int* __restrict__ group_sizes, const int* __restrict__ sched, int G, int M, int K,
+                      int N, float* __restrict__ drhs) {
   using C = TgCfg<BMK_>;
   constexpr int BMK = C::BMK, BNN = C::BNN, kChunk = C::kChunk, kStagesG = C::kStages, kStageG = C::kStage;
   constexpr int kAStage = C::kAStage, kBStage = C::kBStage, kALoadsG = C::kALoads, kBLoadsG = C::kBLoads;
@@ -540,8 +634,16 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* g_start = reinterpret_cast<int*>(smem + C::kLds);
   int* p_base = g_start + G + 1;
+  uint16_t* i_off = reinterpret_cast<uint16_t*>(p_base + G + 1);   // o_g of the item deal
   PairTable pt{g_start, p_base};
   build_pair_table(group_sizes, G, M, pt, nullptr);
+  const int per_g = (K / BMK) * (N / BNN);
+  const int nb = gridDim.x;
+  for (int g = threadIdx.x; g < G; g += C::kThreads) {
+    // reduced mod nb whatever the workspace holds, so every item index stays in range
+    int o = sched != nullptr ? sched[g] % nb : (int)((long long)g * per_g % nb);
+    i_off[g] = (uint16_t)(o < 0 ? o + nb : o);
+  }
   __syncthreads();
   auto nchunks = [&](int g, int p) {
     int r0, r1;
@@ -552,14 +654,15 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave >> 1, wn = wave & 1;
-  const int kt_n = K / BMK, nt_n = N / BNN;
-  const int per_g = kt_n * nt_n;
-  // work item = (expert, n tile, k tile fastest); block b takes items b,
-  // b + gridDim.x, ...  Items of one expert are spread over every block (and
-  // so over every XCD), which keeps the work balanced however skewed the
-  // expert sizes are.
-  const int total = G * per_g;
-  const int stride = gridDim.x;
+  const int kt_n = K / BMK;
+  // work item j of expert g = (n tile j / kt_n, k tile j % kt_n); it goes to
+  // block (o_g + j) mod nb (see build_item_schedule), so a block walks the
+  // experts in order and takes every nb-th item of each from its first one.
+  // Items of one expert are spread over every block (and so over every XCD).
+  auto first_j = [&](int g) {
+    const int j = (int)blockIdx.x - (int)i_off[g];
+    return __builtin_amdgcn_readfirstlane(j < 0 ? j + nb : j);
+  };
 
   // ---- per-lane copy offsets within a chunk (item-independent part) and operand read offsets
   uint32_t va[kALoadsG], vb[kBLoadsG];
@@ -587,19 +690,22 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   const int sd_rd = kAStage + kBStage + 4 * BMK + 4 * (wn * 64 + 4 * (lane >> 4));
 
   // ---- copy side: the next (item, pair, chunk) to copy, stages run ahead of the compute side
-  int ii = blockIdx.x, ig = 0, ikt = 0, int_ = 0, ip = 0, ip1 = 0, ic = 0, inc = 0, irows = 0;
+  int ig = 0, ij = first_j(0), ikt = 0, int_ = 0, ip = 0, ip1 = 0, ic = 0, inc = 0, irows = 0;
   auto pair_pad_rows = [&](int g, int p) {
     int r0, r1;
     pair_rows(pt, g, p, r0, r1);
     return __builtin_amdgcn_readfirstlane((r1 - r0 + kSub - 1) / kSub * kSub);
   };
-  auto seek = [&]() {   // first item at or after ii that has rows
-    while (ii < total && p_base[ii / per_g + 1] == p_base[ii / per_g]) ii += stride;   // expert without rows
-    if (ii < total) {
-      ig = __builtin_amdgcn_readfirstlane(ii / per_g);
-      const int rem = ii % per_g;
-      ikt = rem % kt_n;
-      int_ = rem / kt_n;
+  auto seek = [&]() {   // first item at or after (ig, ij) whose expert has rows
+    while (ig < G && (ij >= per_g || p_base[ig + 1] == p_base[ig])) {
+      ++ig;
+      if (ig < G) ij = first_j(ig);
+    }
+    if (ig < G) {
+      ig = __builtin_amdgcn_readfirstlane(ig);
+      ij = __builtin_amdgcn_readfirstlane(ij);
+      ikt = ij % kt_n;
+      int_ = ij / kt_n;
       ip = __builtin_amdgcn_readfirstlane(p_base[ig]);
       ip1 = __builtin_amdgcn_readfirstlane(p_base[ig + 1]);
       ic = 0;
@@ -652,7 +758,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
     if (++ic == inc) {
       ic = 0;
       if (++ip == ip1) {
-        ii += stride;
+        ij += nb;
         seek();
         set_item_offsets();
       } else {
@@ -673,7 +779,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
   };
   seek();
   set_item_offsets();
-  for (int t = 0; t < kStagesG - 1 && ii < total; ++t) issue();
+  for (int t = 0; t < kStagesG - 1 && ig < G; ++t) issue();
 
   // ---- compute side
   v4f tot[4][4], part[4][4];
@@ -685,10 +791,9 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
       part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
   int tC = 0;
-  for (int ci = blockIdx.x; ci < total; ci += stride) {
-    const int g = __builtin_amdgcn_readfirstlane(ci / per_g);
-    const int rem = ci % per_g;
-    const int kt = rem % kt_n, nt = rem / kt_n;
+  for (int g = 0; g < G; ++g)
+  for (int j = first_j(g); j < per_g; j += nb) {
+    const int kt = j % kt_n, nt = j / kt_n;
     const int p_end = __builtin_amdgcn_readfirstlane(p_base[g + 1]);
     for (int p = __builtin_amdgcn_readfirstlane(p_base[g]); p < p_end; ++p) {
       // the pair's rows padded to 32: its last chunk runs only the sub-steps they cover
@@ -706,7 +811,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
         else if (pending >= 1) wait_vmem_lds<kLoadsG>();
         else wait_vmem_lds<0>();
         barrier_only();
-        const bool copy = ii < total;
+        const bool copy = ig < G;
         uint8_t* wr = smem + (tI % kStagesG) * kStageG;
         const uint8_t* rd = smem + (tC % kStagesG) * kStageG;
         const int nsub = min(kChunk, rpad - c * kChunk) / kSub;
@@ -756,36 +861,53 @@ size_t tgmm_workspace_bytes(long long M, long long K, long long N, int G) {
   const size_t a = 256;
   auto al = [&](size_t x) { return (x + a - 1) / a * a; };
   return al((size_t)tmax * kTileM * K) + al((size_t)tmax * kTileM * N) + al((size_t)tmax * K * 4) +
-         al((size_t)tmax * N * 4);
+         al((size_t)tmax * N * 4) + al((size_t)G * 4);
 }
 
 namespace {
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
+// The GEMM's launch geometry: k-tile rows, ring-stage rows, items per expert, blocks.
+struct GemmGeom {
+  int bmk, chunk, per_g, nb;
+};
+GemmGeom gemm_geom(int G, int K, int N) {
+  GemmGeom q;
+  q.bmk = K % 256 == 0 ? 256 : 128;
+  q.chunk = q.bmk == 256 ? TgCfg<256>::kChunk : TgCfg<128>::kChunk;
+  const int per_cu = q.bmk == 256 ? TgCfg<256>::kBlocksPerCU : TgCfg<128>::kBlocksPerCU;
+  q.per_g = (K / q.bmk) * (N / TgCfg<256>::BNN);
+  // persistent: as many blocks as stay resident at once
+  q.nb = (int)std::min<long long>((long long)G * q.per_g, (long long)per_cu * device_cu_count());
+  return q;
+}
+// Whether the prep pass computes the item deal for this geometry (else the GEMM deals round-robin).
+bool schedule_fits(int G, const GemmGeom& q) { return G <= kMaxSchedGroups && q.nb <= kMaxSchedBlocks && q.nb >= 1; }
+
 template <int BMK>
 hipError_t launch_tgmm_gemm_bmk(const uint8_t* ql, const uint8_t* qd, const float* sl, const float* sd,
-                                const int* group_sizes, int G, int M, int K, int N, bool grad_e5m2, float* drhs,
-                                hipStream_t stream) {
+                                const int* group_sizes, const int* sched, int G, int M, int K, int N, int nb,
+                                bool grad_e5m2, float* drhs, hipStream_t stream) {
   using C = TgCfg<BMK>;
-  const size_t lds = C::kLds + sizeof(int) * 2 * ((size_t)G + 1);
-  const long long items = (long long)G * (K / BMK) * (N / C::BNN);
-  // persistent: as many blocks as stay resident at once
-  const dim3 grid((unsigned)std::min<long long>(items, (long long)C::kBlocksPerCU * device_cu_count()));
+  const size_t lds = C::kLds + sizeof(int) * 2 * ((size_t)G + 1) + sizeof(uint16_t) * (size_t)G;
+  const dim3 grid((unsigned)nb);
   if (grad_e5m2)
     hipLaunchKernelGGL((tgmm_gemm_kernel<true, BMK>), grid, dim3(C::kThreads), lds, stream, ql, qd, sl, sd,
-                       group_sizes, G, M, K, N, drhs);
+                       group_sizes, sched, G, M, K, N, drhs);
   else
     hipLaunchKernelGGL((tgmm_gemm_kernel<false, BMK>), grid, dim3(C::kThreads), lds, stream, ql, qd, sl, sd,
-                       group_sizes, G, M, K, N, drhs);
+                       group_sizes, sched, G, M, K, N, drhs);
   return hipGetLastError();
 }
 
+// sched: the item deal the prep pass wrote, or null for the round-robin deal.
 hipError_t launch_tgmm_gemm(const uint8_t* ql, const uint8_t* qd, const float* sl, const float* sd,
-                            const int* group_sizes, int G, int M, int K, int N, bool grad_e5m2, float* drhs,
-                            hipStream_t stream) {
-  if (K % 256 == 0)
-    return launch_tgmm_gemm_bmk<256>(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
-  return launch_tgmm_gemm_bmk<128>(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
+                            const int* group_sizes, const int* sched, int G, int M, int K, int N, bool grad_e5m2,
+                            float* drhs, hipStream_t stream) {
+  const GemmGeom q = gemm_geom(G, K, N);
+  if (q.bmk == 256)
+    return launch_tgmm_gemm_bmk<256>(ql, qd, sl, sd, group_sizes, sched, G, M, K, N, q.nb, grad_e5m2, drhs, stream);
+  return launch_tgmm_gemm_bmk<128>(ql, qd, sl, sd, group_sizes, sched, G, M, K, N, q.nb, grad_e5m2, drhs, stream);
 }
 }  // namespace
 
@@ -811,6 +933,9 @@ hipError_t launch_tgmm_dense(const uint16_t* lhs, const uint16_t* dout, const in
   uint8_t* qDd = reinterpret_cast<uint8_t*>(srow) + al256((size_t)M * 4);
   float* partial = reinterpret_cast<float*>(qDd + al256((size_t)M * N));
   float* scol = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(partial) + al256((size_t)rc * N * 4));
+  int* sched = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sd) + al256((size_t)tmax * N * 4));
+  const GemmGeom q = gemm_geom(G, K, N);
+  const bool use_sched = M > 0 && tmax > 0 && schedule_fits(G, q);
   if (dbg_srow) srow = dbg_srow;
   if (dbg_scol) scol = dbg_scol;
   if (M > 0) {
@@ -826,11 +951,13 @@ hipError_t launch_tgmm_dense(const uint16_t* lhs, const uint16_t* dout, const in
       hipLaunchKernelGGL(dense_quant_kernel<false>, grid, dim3(256), 0, stream, dout, srow, scol, M, N, qDd);
     if (tmax > 0)
       hipLaunchKernelGGL(dense_gather_kernel, dim3((unsigned)tmax, (unsigned)(K / kPrepCols + N / kPrepCols)),
-                         dim3(kThreads), 0, stream, qLd, qDd, scol, group_sizes, G, M, K, N, ql, qd, sl, sd, status);
+                         dim3(kThreads), 0, stream, qLd, qDd, scol, group_sizes, G, M, K, N, ql, qd, sl, sd, status,
+                         use_sched ? sched : nullptr, q.chunk, q.per_g, q.nb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_tgmm_gemm(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
+  return launch_tgmm_gemm(ql, qd, sl, sd, group_sizes, use_sched ? sched : nullptr, G, M, K, N, grad_e5m2, drhs,
+                          stream);
 }
 
 hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const int* group_sizes, int G, int M, int K,
@@ -844,20 +971,25 @@ hipError_t launch_tgmm_quant(const uint16_t* lhs, const uint16_t* dout, const in
   uint8_t* qd = base + al((size_t)tmax * kTileM * K);
   float* sl = reinterpret_cast<float*>(qd + al((size_t)tmax * kTileM * N));
   float* sd = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sl) + al((size_t)tmax * K * 4));
+  int* sched = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sd) + al((size_t)tmax * N * 4));
+  const GemmGeom q = gemm_geom(G, K, N);
+  const bool use_sched = M > 0 && tmax > 0 && schedule_fits(G, q);
   if (dbg_sl) sl = dbg_sl;
   if (dbg_sd) sd = dbg_sd;
   if (tmax > 0 && M > 0) {
     dim3 grid((unsigned)(K / kPrepCols + N / kPrepCols), (unsigned)tmax);
+    int* sp = use_sched ? sched : nullptr;
     if (grad_e5m2)
       hipLaunchKernelGGL(tgmm_prep_kernel<true>, grid, dim3(kThreads), 0, stream, lhs, dout, group_sizes, G, M, K,
-                         N, ql, qd, sl, sd, status);
+                         N, ql, qd, sl, sd, status, sp, q.chunk, q.per_g, q.nb);
     else
       hipLaunchKernelGGL(tgmm_prep_kernel<false>, grid, dim3(kThreads), 0, stream, lhs, dout, group_sizes, G, M, K,
-                         N, ql, qd, sl, sd, status);
+                         N, ql, qd, sl, sd, status, sp, q.chunk, q.per_g, q.nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_tgmm_gemm(ql, qd, sl, sd, group_sizes, G, M, K, N, grad_e5m2, drhs, stream);
+  return launch_tgmm_gemm(ql, qd, sl, sd, group_sizes, use_sched ? sched : nullptr, G, M, K, N, grad_e5m2, drhs,
+                          stream);
 }
 
 }  // namespace fp8gmm

@@ -238,6 +238,12 @@ int gmm_dswiglu_fp8(const void* dout, const uint8_t* codes, const float* scale, 
  * qL u8 [Tmax][512][K] at byte 0 and qD u8 [Tmax][512][N] at byte
  * A(Tmax*512*K); slab p (p < Tn) holds pair p's rows in order, then zero
  * codes up to the next multiple of 32 rows (later rows are not written).
+ * Next come the pairs' scales (f32 [Tmax][K] at A(Tmax*512*K) + A(Tmax*512*N),
+ * f32 [Tmax][N] after it, A-aligned) and, at byte A(Tmax*512*K) +
+ * A(Tmax*512*N) + A(Tmax*K*4) + A(Tmax*N*4), the GEMM's work-item deal:
+ * int32 [G] block offsets, expert g's work item j (an output tile) going to
+ * GEMM block (offset[g] + j) mod the GEMM's grid.  The deal only balances the
+ * blocks' work; it is written when G <= 256 (else the deal is round-robin).
  */
 int tgmm_quant(const void* lhs, const void* dout, const int32_t* group_sizes, int64_t M, int64_t K, int64_t N,
                int32_t G, int32_t grad_dtype, int32_t tile_m, float* drhs, float* dbg_sL, float* dbg_sD, void* ws,

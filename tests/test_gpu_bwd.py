@@ -396,6 +396,25 @@ def test_tgmm_config4_codes(grad):
     print(f"tgmm config4 {grad}: codes of {n} pairs bit-exact")
 
 
+@pytest.mark.parametrize("cfg,K,N", [(4, 7168, 2048), (3, 7168, 4096), (3, 384, 2048), (2, 2048, 768)])
+def test_tgmm_item_deal(cfg, K, N):
+    """The GEMM's work-item deal that the prep pass writes into the workspace
+    equals the host model's (tests/tgmm_deal.py), integer for integer, for both
+    GEMM geometries (256-row k tiles one block per CU, 128-row two)."""
+    import fp8_moe_grouped_amd as G
+    from tests import tgmm_deal as D
+    gs = np.asarray(W.group_sizes(cfg), np.int32)
+    M, Gn = int(W.SHAPES[cfg]["M"]), len(gs)
+    lhs = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    dout = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(G.OP_TGMM, M, K, N, Gn, 512), dtype=torch.uint8, device="cuda")
+    G.tgmm_quant(lhs, dout, dev(gs), "e5m2", 512, workspace=ws)
+    torch.cuda.synchronize()
+    got = G.tgmm_workspace_deal(ws, M, K, N, Gn).cpu().numpy().tolist()
+    want = D.deal(gs, M, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert want is not None and got == want
+
+
 @pytest.mark.parametrize("grad", ["e5m2", "e4m3"])
 def test_tgmm_every_code(grad):
     """Every finite code of both operands passes through the GEMM: row 0 holds
