@@ -645,10 +645,22 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
     i_off[g] = (uint16_t)(o < 0 ? o + nb : o);
   }
   __syncthreads();
-  auto nchunks = [&](int g, int p) {
-    int r0, r1;
-    pair_rows(pt, g, p, r0, r1);
-    return (r1 - r0 + kChunk - 1) / kChunk;
+  // An expert's first row, end and first pair, read from the table once per
+  // expert; a pair's rows are then scalar arithmetic (no LDS read and wait).
+  struct ExpRows {
+    int s, e, pb;
+  };
+  auto exp_rows = [&](int g) {
+    ExpRows x;
+    x.s = __builtin_amdgcn_readfirstlane(g_start[g]);
+    x.e = __builtin_amdgcn_readfirstlane(g_start[g + 1]);
+    x.pb = __builtin_amdgcn_readfirstlane(p_base[g]);
+    return x;
+  };
+  auto rows_of = [&](const ExpRows& x, int p, int& r0, int& r1) {   // as pair_rows
+    const int tile = x.s / kTileM + (p - x.pb);
+    r0 = max(x.s, tile * kTileM);
+    r1 = min(x.e, (tile + 1) * kTileM);
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -691,10 +703,12 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
 
   // ---- copy side: the next (item, pair, chunk) to copy, stages run ahead of the compute side
   int ig = 0, ij = first_j(0), ikt = 0, int_ = 0, ip = 0, ip1 = 0, ic = 0, inc = 0, irows = 0;
-  auto pair_pad_rows = [&](int g, int p) {
+  ExpRows ix{0, 0, 0};
+  auto set_pair = [&]() {   // chunks and padded rows of the copy side's pair ip
     int r0, r1;
-    pair_rows(pt, g, p, r0, r1);
-    return __builtin_amdgcn_readfirstlane((r1 - r0 + kSub - 1) / kSub * kSub);
+    rows_of(ix, ip, r0, r1);
+    irows = (r1 - r0 + kSub - 1) / kSub * kSub;
+    inc = (irows + kChunk - 1) / kChunk;
   };
   auto seek = [&]() {   // first item at or after (ig, ij) whose expert has rows
     while (ig < G && (ij >= per_g || p_base[ig + 1] == p_base[ig])) {
@@ -706,11 +720,11 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
       ij = __builtin_amdgcn_readfirstlane(ij);
       ikt = ij % kt_n;
       int_ = ij / kt_n;
-      ip = __builtin_amdgcn_readfirstlane(p_base[ig]);
+      ix = exp_rows(ig);
+      ip = ix.pb;
       ip1 = __builtin_amdgcn_readfirstlane(p_base[ig + 1]);
       ic = 0;
-      inc = __builtin_amdgcn_readfirstlane(nchunks(ig, ip));
-      irows = pair_pad_rows(ig, ip);
+      set_pair();
     }
   };
   int tI = 0;
@@ -762,8 +776,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
         seek();
         set_item_offsets();
       } else {
-        inc = __builtin_amdgcn_readfirstlane(nchunks(ig, ip));
-        irows = pair_pad_rows(ig, ip);
+        set_pair();
       }
     }
   };
@@ -791,15 +804,16 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
       part[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
   int tC = 0;
-  for (int g = 0; g < G; ++g)
-  for (int j = first_j(g); j < per_g; j += nb) {
-    const int kt = j % kt_n, nt = j / kt_n;
-    const int p_end = __builtin_amdgcn_readfirstlane(p_base[g + 1]);
-    for (int p = __builtin_amdgcn_readfirstlane(p_base[g]); p < p_end; ++p) {
+  for (int g = 0; g < G; ++g) {
+  const ExpRows cx = exp_rows(g);
+  const int p_end = __builtin_amdgcn_readfirstlane(p_base[g + 1]);
+  for (int it = first_j(g); it < per_g; it += nb) {
+    const int kt = it % kt_n, nt = it / kt_n;
+    for (int p = cx.pb; p < p_end; ++p) {
       // the pair's rows padded to 32: its last chunk runs only the sub-steps they cover
       int pr0, pr1;
-      pair_rows(pt, g, p, pr0, pr1);
-      const int rpad = __builtin_amdgcn_readfirstlane((pr1 - pr0 + kSub - 1) / kSub * kSub);
+      rows_of(cx, p, pr0, pr1);
+      const int rpad = (pr1 - pr0 + kSub - 1) / kSub * kSub;
       const int nc = (rpad + kChunk - 1) / kChunk;
       for (int c = 0; c < nc; ++c, ++tC) {
         // stage tC landed in every wave's copy (only the copies issued after
@@ -850,6 +864,7 @@ void tgmm_gemm_kernel(const uint8_t* __restrict__ ql, const uint8_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 4; ++j) tot[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
+  }
   }
 }
 
