@@ -44,8 +44,8 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # x 2.0, WRITE_SIZE x 1.0 (MiB read, MiB written).  Each entry holds the hash of the kernel's sources when
 # the counters were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 2633, 77),
-    "wo_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 1308, 269),
+    "wi_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 2648, 77),
+    "wo_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 1309, 269),
     "wi_dlhs": ("dlhs.hip", "8935edf5202e04f8", 2815, 269),
     "wo_dlhs": ("dlhs.hip", "8935edf5202e04f8", 1427, 77),
     "tgmm": ("tgmm.hip", "c350ea6b3968908a", 346 + 1398, 181 + 1792),
