@@ -48,7 +48,7 @@ MEASURED_TRAFFIC_MIB = {
     "wo_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 1309, 269),
     "wi_dlhs": ("dlhs.hip", "8935edf5202e04f8", 2815, 269),
     "wo_dlhs": ("dlhs.hip", "8935edf5202e04f8", 1427, 77),
-    "tgmm": ("tgmm.hip", "c350ea6b3968908a", 346 + 1398, 181 + 1792),
+    "tgmm": ("tgmm.hip", "b4a5c32496ccabb6", 346 + 1398, 181 + 1792),
     "dequant": ("dequant.hip", "f9f30637c789a9b5", 455, 896),
     "wi_quant": ("quant.hip", "684bab8ddb83acb4", 269, 135),
     "wo_quant": ("quant.hip", "684bab8ddb83acb4", 77, 39),
