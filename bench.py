@@ -44,14 +44,14 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 # x 2.0, WRITE_SIZE x 1.0 (MiB read, MiB written).  Each entry holds the hash of the kernel's sources when
 # the counters were taken; once the sources change the figure no longer applies and traffic is null.
 MEASURED_TRAFFIC_MIB = {
-    "wi_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 2648, 77),
-    "wo_gemm": ("gmm_fwd.hip", "080ddf0a87054686", 1309, 269),
-    "wi_dlhs": ("dlhs.hip", "8935edf5202e04f8", 2815, 269),
-    "wo_dlhs": ("dlhs.hip", "8935edf5202e04f8", 1427, 77),
-    "tgmm": ("tgmm.hip", "b4a5c32496ccabb6", 346 + 1398, 181 + 1792),
-    "dequant": ("dequant.hip", "f9f30637c789a9b5", 455, 896),
-    "wi_quant": ("quant.hip", "684bab8ddb83acb4", 269, 135),
-    "wo_quant": ("quant.hip", "684bab8ddb83acb4", 77, 39),
+    "wi_gemm": ("gmm_fwd.hip", "f0b71cf866345648", 2620, 77),
+    "wo_gemm": ("gmm_fwd.hip", "f0b71cf866345648", 1307, 269),
+    "wi_dlhs": ("dlhs.hip", "4745e5e8785bab26", 2814, 269),
+    "wo_dlhs": ("dlhs.hip", "4745e5e8785bab26", 1427, 77),
+    "tgmm": ("tgmm.hip", "2423c5c4f52c4400", 346 + 1437, 181 + 1792),
+    "dequant": ("dequant.hip", "8efe77d827d0d814", 455, 896),
+    "wi_quant": ("quant.hip", "924b9abefe895b12", 269, 135),
+    "wo_quant": ("quant.hip", "924b9abefe895b12", 77, 39),
 }
 
 

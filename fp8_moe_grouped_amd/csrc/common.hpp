@@ -121,6 +121,8 @@ __device__ __forceinline__ v2i lds_read_tr8(const void* p) {
 
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 
+constexpr int kCpolStream = 2;   // buffer-load cache policy: streaming (non-temporal)
+
 // Raw buffer resource over [base, base + bytes); loads at or past the end
 // return zeros instead of touching memory.
 __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {

@@ -16,8 +16,6 @@
 
 namespace fp8gmm {
 
-constexpr int kCpolStream = 2;   // buffer-load cache policy: streaming (non-temporal)
-
 __device__ __forceinline__ float round_to_bf16(float v) {
   return __builtin_bit_cast(float, pack_bf16x2(v, 0.f) << 16);
 }

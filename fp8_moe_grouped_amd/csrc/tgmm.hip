@@ -237,25 +237,35 @@ __global__ __launch_bounds__(kThreads) void tgmm_prep_kernel(const uint16_t* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = tid & 7;          // 8-column group
   const int rr = tid >> 3;         // 0..31
-  // ---- load the pair's rows (16 per thread) and reduce the column amax
+  // ---- load the pair's rows (16 per thread) and reduce the column amax.
+  // Every load goes out before any is used: a row group past the pair's rows
+  // is skipped by a wave-uniform branch, and the rows of the last group past
+  // the pair's end read zeros through a buffer range that ends there.
+  const BufRsrc rsrc = make_rsrc(src + (size_t)r0 * cols, (uint32_t)R * (uint32_t)cols * 2u);
+  const int n_it = (R + 31) / 32;
   v4i x[16];
   float am[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) am[e] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int r = rr + 32 * i;
-    if (r < R) {
-      x[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + (size_t)(r0 + r) * cols + c0 + cg * 8));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        am[2 * e] = __builtin_fmaxf(am[2 * e], __builtin_fabsf(bf16_lo((uint32_t)x[i][e])));
-        am[2 * e + 1] = __builtin_fmaxf(am[2 * e + 1], __builtin_fabsf(bf16_hi((uint32_t)x[i][e])));
-      }
-    } else {
+    if (i < n_it)
+      x[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rsrc, (uint32_t)((rr + 32 * i) * cols + c0 + cg * 8) * 2u, 0u, kCpolStream));
+    else
       x[i] = (v4i){0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      am[2 * e] = __builtin_fmaxf(am[2 * e], __builtin_fabsf(bf16_lo((uint32_t)x[i][e])));
+      am[2 * e + 1] = __builtin_fmaxf(am[2 * e + 1], __builtin_fabsf(bf16_hi((uint32_t)x[i][e])));
     }
   }
+  // the quantize pass widens the raw rows again instead of keeping these f32 values
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[i]));
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float v = am[e];
